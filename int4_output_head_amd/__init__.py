@@ -1,0 +1,15 @@
+"""MI355X-native int4 lm_head speculative verification.
+
+The compute path is the HIP library built from ``csrc/`` (gfx950 only); the
+Python entry points below marshal torch tensors into its C ABI.  Importing
+this package loads nothing; the library is loaded on the first call.
+"""
+
+__all__ = ["verify", "verify_batch", "check_weights", "workspace_bytes", "load_library"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,300 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test checks the oracle against something fixed independently of it:
+hand-derived values (tests/golden/hand_cases.json), exact rational
+arithmetic, integer arithmetic in a regime where binary32 is exact, library
+routines (numpy's binary16 conversion, numpy.argmax), and invariants of the
+definition (negation, permutation, power-of-two scaling, zero scales, one-hot
+inputs, acceptance rules).
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from int4_output_head_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+@pytest.fixture(scope="module")
+def hand():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ formats
+
+def test_half_to_double_all_patterns(oracle_mod):
+    """All 65536 binary16 patterns against numpy's conversion."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([oracle_mod.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_unpack_hand_fixture(oracle_mod, hand):
+    c = hand["unpack"]
+    q, nbad = oracle_mod.unpack(np.array(c["bytes"], np.uint8), c["V"], c["H"])
+    assert nbad == 0
+    assert q.ravel().tolist() == c["q"]
+
+
+def test_bad_nibble_rejected(oracle_mod, hand):
+    c = hand["bad_nibble"]
+    b = np.array(c["bytes"], np.uint8)
+    _, nbad = oracle_mod.unpack(b, c["V"], c["H"])
+    assert nbad == c["n_bad"]
+    assert oracle_mod.count_bad_nibbles(b, c["V"], c["H"]) == c["n_bad"]
+    x = np.full((1, c["H"]), 0x3C00, np.uint16)
+    s = np.full(c["H"], 0x3C00, np.uint16)
+    with pytest.raises(oracle_mod.OracleError) as e:
+        oracle_mod.logits(x, b, s, 1, c["V"], c["H"])
+    assert e.value.status == oracle_mod.EWEIGHT
+
+
+def test_nonfinite_rejected(oracle_mod):
+    d = synth.uniform_inputs(2, 4, 8, seed=1)
+    x = d["hidden"].copy()
+    x[1, 3] = 0x7C00  # +inf
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.logits(x, d["packed"], d["scales"], 2, 4, 8)
+    s = d["scales"].copy()
+    s[0] = 0x7E00  # NaN
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.logits(d["hidden"], d["packed"], s, 2, 4, 8)
+
+
+def test_pack_unpack_roundtrip(oracle_mod):
+    rng = np.random.default_rng(5)
+    q = rng.integers(-7, 8, size=(33, 64), dtype=np.int8)
+    q2, nbad = oracle_mod.unpack(synth.pack_int4(q), 33, 64)
+    assert nbad == 0 and np.array_equal(q, q2)
+
+
+# ------------------------------------------------------------------ rounding
+
+def _hand_logit(oracle_mod, c):
+    H = c["H"]
+    x = np.array(c["hidden"], np.uint16).reshape(1, H)
+    s = np.array(c["scales"], np.uint16)
+    w = np.array(c["bytes"], np.uint8).reshape(1, H // 2)
+    return oracle_mod.logits(x, w, s, 1, 1, H)[0, 0], oracle_mod.logit_one(x[0], w[0], s, H)
+
+
+def test_sum_order_is_ascending_h(oracle_mod, hand):
+    for c in hand["sum_order"]:
+        a, b = _hand_logit(oracle_mod, c)
+        want = np.float32(Fraction(c["logit_num"], c["logit_den"]))
+        assert a == want and b == want
+
+
+def test_products_rounded_separately(oracle_mod, hand):
+    c = hand["separate_rounding"]
+    a, b = _hand_logit(oracle_mod, c)
+    want = Fraction(c["logit_num"], c["logit_den"])
+    fused = Fraction(c["fused_num"], c["fused_den"])
+    assert Fraction(float(a)) == want and Fraction(float(b)) == want
+    assert want != fused
+
+
+# ------------------------------------------------------------------ exact arithmetic
+
+def _exact_logits(q, x_bits, s_bits):
+    x = [[Fraction(float(v)) for v in row] for row in x_bits.view(np.float16).astype(np.float64)]
+    s = [Fraction(float(v)) for v in s_bits.view(np.float16).astype(np.float64)]
+    M, V = len(x), q.shape[0]
+    H = q.shape[1]
+    ex = [[sum(x[r][h] * s[h] * int(q[v, h]) for h in range(H)) for v in range(V)]
+          for r in range(M)]
+    ab = [[sum(abs(x[r][h] * s[h] * int(q[v, h])) for h in range(H)) for v in range(V)]
+          for r in range(M)]
+    return ex, ab
+
+
+@pytest.mark.parametrize("seed,M,V,H", [(0, 2, 9, 16), (1, 3, 17, 64), (2, 4, 40, 32),
+                                        (3, 1, 64, 64)])
+def test_brute_force_exact_rational(oracle_mod, seed, M, V, H):
+    """Oracle logits within the binary32 summation bound of the exact sum;
+    argmax equals the exact argmax wherever the exact top-2 gap exceeds twice
+    that bound."""
+    d = synth.uniform_inputs(M, V, H, seed=seed, heavy_frac=0.1)
+    lg = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H)
+    ex, ab = _exact_logits(d["q"], d["hidden"], d["scales"])
+    u = Fraction(1, 2 ** 24)
+    # products are rounded once and the sum H-1 times: gamma_H = H u / (1 - H u)
+    gam = H * u / (1 - H * u)
+    idx, mx, gap, amax = oracle_mod.argmax_rows(lg)
+    for r in range(M):
+        bounds = []
+        for v in range(V):
+            bound = gam * ab[r][v]
+            assert abs(Fraction(float(lg[r, v])) - ex[r][v]) <= bound
+            bounds.append(bound)
+        order = sorted(range(V), key=lambda v: (-ex[r][v], v))
+        if V > 1 and ex[r][order[0]] - ex[r][order[1]] > 2 * max(bounds):
+            assert idx[r] == order[0]
+
+
+@pytest.mark.parametrize("seed,M,V,H", [(0, 4, 300, 128), (1, 16, 257, 512), (2, 3, 64, 5120)])
+def test_integer_exact_mode(oracle_mod, seed, M, V, H):
+    """x integer, s in {1, 1/2, 1/4}: every partial sum is exact, so the oracle
+    must equal integer arithmetic bit for bit, and its argmax (with exact ties)
+    must equal numpy.argmax (first maximum)."""
+    d = synth.int_exact_inputs(M, V, H, seed)
+    lg = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H)
+    x4 = (d["hidden"].view(np.float16).astype(np.float64) * 1).astype(np.int64)
+    s4 = (d["scales"].view(np.float16).astype(np.float64) * 4).astype(np.int64)
+    exact4 = (x4 * s4[None, :]) @ d["q"].astype(np.int64).T  # 4 * logit, exact
+    assert np.array_equal(lg, (exact4 / 4.0).astype(np.float32))
+    idx, mx, _, _ = oracle_mod.argmax_rows(lg)
+    assert np.array_equal(idx, np.argmax(exact4, axis=1))
+    assert np.array_equal(mx, lg[np.arange(M), idx])
+
+
+def test_int_exact_ties_lowest_index(oracle_mod):
+    """Duplicate the best row at a higher index: the lower index must win;
+    duplicate it at a lower index: the argmax moves down."""
+    M, V, H = 2, 50, 64
+    d = synth.int_exact_inputs(M, V, H, 7)
+    q = d["q"].copy()
+    lg = oracle_mod.logits(d["hidden"], synth.pack_int4(q), d["scales"], M, V, H)
+    b0 = int(np.argmax(lg[0]))
+    q2 = q.copy()
+    q2[V - 1] = q[b0]
+    q2[0] = q[b0]
+    lg2 = oracle_mod.logits(d["hidden"], synth.pack_int4(q2), d["scales"], M, V, H)
+    idx, _, gap, _ = oracle_mod.argmax_rows(lg2)
+    assert idx[0] == 0 and gap[0] == 0.0
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_one_hot_hidden(oracle_mod):
+    M, V, H = 3, 120, 64
+    d = synth.uniform_inputs(M, V, H, seed=11)
+    ks = [0, 31, 63]
+    x = np.zeros((M, H))
+    for r, k in enumerate(ks):
+        x[r, k] = 1.0
+    xb = synth.f16_bits(x)
+    lg = oracle_mod.logits(xb, d["packed"], d["scales"], M, V, H)
+    s = d["scales"].view(np.float16).astype(np.float32)
+    for r, k in enumerate(ks):
+        assert np.array_equal(lg[r], d["q"][:, k].astype(np.float32) * s[k])
+    idx, _, _, _ = oracle_mod.argmax_rows(lg)
+    for r, k in enumerate(ks):
+        assert idx[r] == int(np.argmax(d["q"][:, k]))
+
+
+def test_zero_scales(oracle_mod):
+    M, V, H, T = 4, 77, 96, 4
+    d = synth.uniform_inputs(M, V, H, seed=12)
+    s0 = np.zeros(H, np.uint16)
+    drafts = np.array([[0, 0, 5]], np.int32)
+    out = oracle_mod.verify(d["hidden"], d["packed"], s0, drafts, 1, T, V, H, want_logits=True)
+    assert np.all(out["logits"] == 0.0)
+    assert np.all(out["argmax_ids"] == 0) and np.all(out["logits_max"] == 0.0)
+    assert out["n_accepted"][0] == 2
+    # one zero scale == that hidden channel zeroed
+    s1 = d["scales"].copy()
+    s1[17] = 0
+    x1 = d["hidden"].copy()
+    x1[:, 17] = 0
+    a = oracle_mod.logits(d["hidden"], d["packed"], s1, M, V, H)
+    b = oracle_mod.logits(x1, d["packed"], d["scales"], M, V, H)
+    assert np.array_equal(a, b)
+
+
+def test_negation(oracle_mod):
+    M, V, H = 3, 200, 128
+    d = synth.uniform_inputs(M, V, H, seed=13)
+    a = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H)
+    b = oracle_mod.logits(d["hidden"], synth.pack_int4(-d["q"]), d["scales"], M, V, H)
+    assert np.array_equal(a, -b)  # == treats -0.0 and +0.0 as equal
+    ia, _, _, _ = oracle_mod.argmax_rows(a)
+    ib, _, _, _ = oracle_mod.argmax_rows(-b)
+    assert np.array_equal(ia, ib)
+
+
+def test_row_permutation(oracle_mod):
+    M, V, H = 2, 150, 64
+    d = synth.uniform_inputs(M, V, H, seed=14)
+    perm = np.random.default_rng(3).permutation(V)
+    a = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H)
+    b = oracle_mod.logits(d["hidden"], d["packed"][perm], d["scales"], M, V, H)
+    assert np.array_equal(a[:, perm], b)
+
+
+def test_power_of_two_scaling(oracle_mod):
+    M, V, H = 2, 100, 64
+    d = synth.uniform_inputs(M, V, H, seed=15)
+    x2 = synth.f16_bits(d["hidden"].view(np.float16).astype(np.float64) * 4.0)
+    a = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H)
+    b = oracle_mod.logits(x2, d["packed"], d["scales"], M, V, H)
+    assert np.array_equal(a * 4.0, b)
+
+
+def test_thread_count_invariance(oracle_mod):
+    M, V, H = 4, 333, 256
+    d = synth.uniform_inputs(M, V, H, seed=16)
+    a = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H, n_threads=1)
+    b = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H, n_threads=4)
+    assert np.array_equal(a, b)
+
+
+def test_logit_one_matches_batched(oracle_mod):
+    """The per-product form (x*s)*q and the precomputed x*s form agree bit
+    for bit (x*s is exact in binary32)."""
+    M, V, H = 2, 20, 5120
+    d = synth.uniform_inputs(M, V, H, seed=17)
+    lg = oracle_mod.logits(d["hidden"], d["packed"], d["scales"], M, V, H)
+    for r in range(M):
+        for v in (0, 7, 19):
+            assert oracle_mod.logit_one(d["hidden"][r], d["packed"][v], d["scales"], H) == lg[r, v]
+
+
+# ------------------------------------------------------------------ acceptance
+
+def test_acceptance_rules(oracle_mod):
+    am = np.array([5, 9, 2, 7, 1], np.int32)  # T = 5
+    T = 5
+    assert oracle_mod.accept(am, am[:4], 1, T)[0] == 4          # all drafts right: T-1
+    for k in range(4):
+        d = am[:4].copy()
+        d[k] = 1000 + k                                         # first mismatch at k
+        d[k + 1:] = am[k + 1:4]
+        assert oracle_mod.accept(am, d, 1, T)[0] == k
+    assert oracle_mod.accept(np.array([3], np.int32), None, 1, 1)[0] == 0   # T == 1
+    d = np.array([-1, 9, 2, 7], np.int32)                       # out-of-range id never matches
+    assert oracle_mod.accept(am, d, 1, T)[0] == 0
+    # later matches after a mismatch do not count
+    d = np.array([5, 0, 2, 7], np.int32)
+    assert oracle_mod.accept(am, d, 1, T)[0] == 1
+    # several requests
+    am2 = np.concatenate([am, am])
+    d2 = np.stack([am[:4], np.array([5, 9, 0, 0], np.int32)])
+    assert oracle_mod.accept(am2, d2, 2, T).tolist() == [4, 2]
+
+
+def test_verify_end_to_end_consistency(oracle_mod):
+    """verify() equals logits() + argmax_rows() + accept() composed."""
+    cfg = synth.CONFIGS["tiny"]
+    head = synth.make_head(cfg)
+    x = synth.make_hidden(cfg, 0)
+    lg = oracle_mod.logits(x, head["packed"], head["scales"], cfg.M, cfg.V, cfg.H)
+    idx, mx, _, _ = oracle_mod.argmax_rows(lg)
+    plan = synth.draft_plan(cfg, 0)
+    drafts = synth.finalize_drafts(cfg, plan, idx)
+    out = oracle_mod.verify(x, head["packed"], head["scales"], drafts, cfg.R, cfg.T, cfg.V,
+                            cfg.H, want_logits=True)
+    assert np.array_equal(out["logits"], lg)
+    assert np.array_equal(out["argmax_ids"], idx)
+    assert out["n_accepted"][0] >= 2  # the plan copies the first two argmax ids
+    assert np.array_equal(drafts[0, :2], idx[:2])
