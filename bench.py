@@ -1,0 +1,230 @@
+"""Benchmark of the int4 lm_head verify path on one MI355X.
+
+A step is one verify call: the whole path (activation codes, weight stream,
+contraction, argmax, acceptance) over one block of synthetic hidden states,
+with every input already resident in HBM.  The head is rotated over several
+copies so that the 256 MB Infinity Cache cannot serve it.  Prints one JSON
+line.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--config full_t16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+METRIC = "int4 lm_head verify: weight GB/s (% HBM peak) and verified tokens/s at T=16"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def stored_argmax(name):
+    path = os.path.join(ROOT, "tests", "golden", f"argmax_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        return json.load(f)
+
+
+def cpu_baseline(cfg, head, trials, n_threads):
+    """The oracle, as it is, on this host: whole verify steps of the same
+    workload (bounded number of trials)."""
+    from oracle import oracle
+    from int4_output_head_amd import synth
+    times = []
+    for trial in trials:
+        x = synth.make_hidden(cfg, trial)
+        drafts = np.zeros((cfg.R, cfg.T - 1), np.int32)
+        t0 = time.perf_counter()
+        oracle.verify(x, head["packed"], head["scales"], drafts, cfg.R, cfg.T, cfg.V, cfg.H,
+                      n_threads=n_threads)
+        times.append(time.perf_counter() - t0)
+    t = float(np.mean(times))
+    return dict(value=round(cfg.weight_bytes / t / 1e9, 4), unit="GB/s", cores=n_threads,
+                kind="oracle", seconds_per_step=round(t, 4),
+                verified_tok_s=round(cfg.M / t, 3),
+                sample=f"{len(trials)} whole verify steps of the same workload (all {cfg.M} rows x "
+                       f"{cfg.V} vocab rows), trial seeds {list(trials)}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="full_t16")
+    ap.add_argument("--copies", type=int, default=0, help="head copies to rotate (0: auto)")
+    ap.add_argument("--cpu-trials", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path runs on a single MI355X; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from int4_output_head_amd import binding, synth
+
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    binding.load_library()
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} CUs {props.multi_processor_count}; config {cfg.desc}")
+
+    t0 = time.time()
+    head = synth.make_head(cfg)
+    log(f"head generated in {time.time() - t0:.1f}s")
+    copies = args.copies or max(2, -(-600_000_000 // cfg.weight_bytes))  # > 256 MB MALL
+    w0 = torch.from_numpy(head["packed"]).to(dev)
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    s = torch.from_numpy(head["scales"]).view(torch.float16).to(dev)
+
+    stored = stored_argmax(cfg.name)
+    n_trials = min(cfg.trials, 20)
+    xs, ds, ref_ids = [], [], []
+    for trial in range(n_trials):
+        x = synth.make_hidden(cfg, trial)
+        xs.append(torch.from_numpy(x).view(torch.float16).to(dev).reshape(cfg.R, cfg.T, cfg.H))
+        ids = None
+        if stored is not None and str(trial) in stored["trials"]:
+            ids = np.array(stored["trials"][str(trial)]["argmax"], np.int32)
+        ref_ids.append(ids)
+        if cfg.T > 1:
+            base = ids if ids is not None else np.zeros(cfg.M, np.int32)
+            d = synth.finalize_drafts(cfg, synth.draft_plan(cfg, trial), base)
+            ds.append(torch.from_numpy(d).to(dev))
+        else:
+            ds.append(None)
+    if stored is None:
+        log("no stored oracle argmax for this config: drafts are not aligned with the target")
+
+    work = binding.Workspace(binding.workspace_bytes(cfg.R, cfg.T, cfg.V, cfg.H), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        return binding.verify_batch(xs[i % n_trials], ws[i % copies], s, ds[i % n_trials],
+                                    workspace=work)
+
+    # parity gate against the stored oracle argmax (ids may differ only at near ties)
+    gate = dict(rows=0, ids_equal=0, near_tie_rows_allowed=0)
+    for trial in range(n_trials):
+        lmax, amax, nacc = step(trial)
+        if ref_ids[trial] is not None:
+            g = amax.cpu().numpy()
+            gate["rows"] += cfg.M
+            gate["ids_equal"] += int(np.sum(g == ref_ids[trial]))
+            gaps = np.array(stored["trials"][str(trial)]["gap"])
+            am = np.array(stored["trials"][str(trial)]["amax"])
+            gate["near_tie_rows_allowed"] += int(np.sum(gaps < 2e-3 * am))
+    torch.cuda.synchronize()
+    log(f"parity gate vs stored oracle argmax: {gate}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # (1) eager launches, one HIP event pair around each call: the per-launch
+    #     duration of the C-ABI call (both of its kernels) for the roofline
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step(i)
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = t_begin.elapsed_time(t_end) / args.steps
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])  # ms per launch
+
+    # (2) the steps captured in a HIP graph and replayed (how a serving loop
+    #     issues verify steps): whole-job throughput
+    calls_per_graph = min(args.steps, 20)
+    replays = max(1, args.steps // calls_per_graph)
+    cap = torch.cuda.Stream(dev)
+    cap.wait_stream(stream)
+    outs = []
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        step(0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for i in range(calls_per_graph):
+                outs.append(step(i))
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    # every output of the replay equals the eager result of the same step
+    replay_ok = True
+    for i in (0, calls_per_graph - 1):
+        ref = step(i)
+        torch.cuda.synchronize()
+        replay_ok &= all(torch.equal(a, b) for a, b in zip(ref, outs[i]))
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    g0.record(stream)
+    for _ in range(replays):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_steps = replays * calls_per_graph
+    ms_per_step = g0.elapsed_time(g1) / graph_steps
+    committed_tokens = sum(int(o[2].to(torch.int64).sum().item()) + cfg.R for o in outs) * replays
+
+    t_launch = float(per.mean()) * 1e-3
+    wbytes = cfg.weight_bytes
+    value = wbytes / (ms_per_step * 1e-3) / 1e9
+    achieved = wbytes / t_launch / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": graph_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": cfg.desc, "V": cfg.V, "H": cfg.H, "R": cfg.R, "T": cfg.T,
+                   "head_copies_rotated": copies, "trials": n_trials,
+                   "timing": f"HIP graph of {calls_per_graph} steps replayed {replays}x"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "verified_tok_s": round(cfg.M / (ms_per_step * 1e-3), 1),
+        "committed_tok_s": round(committed_tokens / (graph_steps * ms_per_step * 1e-3), 1),
+        "eager": {"ms_per_step": round(eager_ms, 5),
+                  "GB_s": round(wbytes / (eager_ms * 1e-3) / 1e9, 2)},
+        "launch_us": {"mean": round(per.mean() * 1e3, 3), "p10": round(np.percentile(per, 10) * 1e3, 3),
+                      "p50": round(np.percentile(per, 50) * 1e3, 3),
+                      "p90": round(np.percentile(per, 90) * 1e3, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "graph_replay_matches_eager": bool(replay_ok),
+        "parity_gate": gate,
+    }
+    if not args.no_cpu_baseline:
+        n_threads = min(16, os.cpu_count() or 1)
+        log(f"cpu baseline: oracle on {n_threads} threads, {args.cpu_trials} trials")
+        result["cpu_baseline"] = cpu_baseline(cfg, head, list(range(args.cpu_trials)), n_threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+/*
+ * int4vh.h -- C ABI of the MI355X (gfx950) int4 lm_head verification library
+ * (libint4vh.so).
+ *
+ * The operation.  A verify block of final hidden states is projected through
+ * a calibrated int4 output head, each position is reduced to its greedy
+ * argmax, and the number of leading drafted tokens that agree with those
+ * argmaxes is counted:
+ *
+ *   logit[r, v]   = sum_h  f32(hidden[r, h]) * f32(scales[h]) * q[v, h]
+ *   argmax_ids[r] = the v with the largest logit[r, v]; lowest v on ties
+ *   logits_max[r] = logit[r, argmax_ids[r]]
+ *   n_accepted[i] = largest k <= T-1 with draft_ids[i, t] == argmax_ids[i*T + t]
+ *                   for every t < k
+ *
+ * Sources: the int4 head with one scale per hidden channel and values in
+ * [-7, 7] is the requantised lm_head of "Qwen3.8-27B on a Single RTX 3090:
+ * How Calibrated Quantization and Speculative Decoding Hit 1,000 tok/s",
+ * Technical Insight (requantisation listing), also "HyperQwen: 1,000 tok/s on
+ * a Single RTX 3090 Through Aggressive Recurrent-State Speculation", Technical
+ * Insight (lm_head paragraph: only the ordering of logits matters).  Greedy
+ * verification with an accepted prefix is the verify step of the same
+ * "Qwen3.8-27B ..." page, Technical Insight (split-KV verify listing), and a
+ * block of up to 16 positions (7 drafted, up to 8 copied from the context, 1
+ * bonus) is from "HyperQwen on one RTX 3090: a first-time developer's guide to
+ * the 381-token claim", "What actually became faster?".
+ *
+ * Data layout (all row-major, all device memory owned by the caller):
+ *   hidden     binary16 [M, H], M = R*T rows (request i owns rows i*T..i*T+T-1)
+ *   packed_w   uint8 [V, H/2]: two int4 values per byte, low nibble = even
+ *              hidden channel h, high nibble = h+1, two's-complement nibbles.
+ *              Only [-7, 7] is legal; nibble 0x8 is a precondition violation
+ *              that the verify calls do not check (see *_check_weights).
+ *   scales     binary16 [H], one scale per hidden channel
+ *   draft_ids  int32 [R, T-1]; NULL allowed only when T == 1.  Ids outside
+ *              [0, V) are legal and never match.
+ *   logits_max float32 [M]; argmax_ids int32 [M]; n_accepted int32 [R]
+ *   logits_out optional float32 [M, V] (every logit; NULL to skip)
+ *
+ * Numerics.  Products use the exact value of hidden*scale rounded to a
+ * 16-bit fixed-point code per row (a power-of-two step of at most 2^-14 of
+ * the row's largest |hidden*scale|), multiplied by the exact int4 weights in
+ * int8 matrix cores with exact int32 accumulation; each logit is rounded to
+ * binary32 once.  The absolute error of a logit is below
+ * 2^-15 * max_h|hidden*scale| * sum_h|q[v,h]|, and every result is
+ * independent of the launch shape and bit-for-bit reproducible.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
+ * the null stream).  Results are valid once the caller synchronises that
+ * stream.  The verify calls allocate nothing and never synchronise.
+ *
+ * Workspace.  Every verify call needs a caller-owned device workspace of at
+ * least verify_lm_head_int4_workspace_bytes(R, T, V, H) bytes, 256-byte
+ * aligned, initialised once with verify_lm_head_int4_workspace_init.  A
+ * call leaves the workspace ready for the next call.  Two calls that are in
+ * flight at the same time must not share a workspace.  After a call that
+ * returned INT4VH_EHIP, initialise the workspace again.
+ *
+ * Errors.  Every entry point returns a status code; nothing is thrown across
+ * the ABI.  Arguments are validated on the host before anything is launched
+ * (no GPU call happens when validation fails):
+ *   INT4VH_EINVAL       T outside [1, 16]; R < 1; R*T > 16 for the
+ *                       single-block kernels of this version; V < 1; H < 32
+ *                       or H % 32 != 0; a required pointer is NULL
+ *   INT4VH_EALIGN       a tensor pointer is not 16-byte aligned (workspace:
+ *                       256-byte aligned)
+ *   INT4VH_EWORKSPACE   workspace smaller than required
+ *   INT4VH_EUNSUPPORTED a shape beyond this build's limits (H > 8192,
+ *                       V*H/2 >= 2^40 bytes)
+ *   INT4VH_EHIP         a HIP runtime error; the text is in
+ *                       verify_lm_head_int4_last_error()
+ */
+#ifndef INT4VH_H
+#define INT4VH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    INT4VH_OK = 0,
+    INT4VH_EINVAL = -1,
+    INT4VH_EALIGN = -2,
+    INT4VH_EWORKSPACE = -3,
+    INT4VH_EHIP = -4,
+    INT4VH_EUNSUPPORTED = -5
+};
+
+/* Largest hidden size of this build. */
+#define INT4VH_MAX_H 8192
+/* Largest T (verify positions per request). */
+#define INT4VH_MAX_T 16
+
+/* Bytes of workspace a verify call with these sizes needs (0 if the sizes are
+ * invalid).  Pure host function. */
+size_t verify_lm_head_int4_workspace_bytes(int R, int T, int V, int H);
+
+/* Zero the workspace's control words on `stream` (a small fill kernel, no
+ * memset node, so it may be captured in a graph).  Call once after
+ * allocation.  Returns INT4VH_EINVAL for NULL, INT4VH_EALIGN if not 256-byte
+ * aligned, INT4VH_EWORKSPACE if ws_bytes is below the minimum for any call. */
+int verify_lm_head_int4_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/* One request: the verify block of T <= 16 positions (R = 1). */
+int verify_lm_head_int4(const void *hidden, const uint8_t *packed_w, const void *scales,
+                        const int32_t *draft_ids, int T, int V, int H,
+                        float *logits_max, int32_t *argmax_ids, int32_t *n_accepted,
+                        float *logits_out, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* R independent requests of T positions each, sharing one head.  Rows of
+ * request i are hidden[i*T .. i*T+T-1]; its drafts are draft_ids[i*(T-1) ..].
+ * Per-request acceptance goes to n_accepted[i]. */
+int verify_lm_head_int4_batch(const void *hidden, const uint8_t *packed_w, const void *scales,
+                              const int32_t *draft_ids, int R, int T, int V, int H,
+                              float *logits_max, int32_t *argmax_ids, int32_t *n_accepted,
+                              float *logits_out, void *workspace, size_t workspace_bytes,
+                              void *stream);
+
+/* Count illegal nibbles (0x8) of a packed head into *n_bad_out (device int32,
+ * overwritten).  Asynchronous on `stream`. */
+int verify_lm_head_int4_check_weights(const uint8_t *packed_w, int V, int H,
+                                      int32_t *n_bad_out, void *stream);
+
+/* Static text for a status code. */
+const char *verify_lm_head_int4_status_string(int status);
+
+/* Text of the last INT4VH_EHIP error raised on the calling thread ("" if
+ * none).  Valid until the next call on that thread. */
+const char *verify_lm_head_int4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INT4VH_H */

@@ -1,0 +1,867 @@
+// int4vh.hip -- int4 lm_head speculative verification for MI355X (gfx950).
+//
+// One call computes, for a verify block of M <= 16 rows of final hidden
+// states, every logit of a calibrated int4 head, the greedy argmax of each
+// row and the accepted-prefix length of each request.  The head is the
+// requantised lm_head of "Qwen3.8-27B on a Single RTX 3090: How Calibrated
+// Quantization and Speculative Decoding Hit 1,000 tok/s", Technical Insight
+// (values in [-7, 7], one scale per hidden channel); the greedy compare of a
+// drafted block is the verify step of the same section; blocks of up to 16
+// positions are from "HyperQwen on one RTX 3090: a first-time developer's
+// guide to the 381-token claim", "What actually became faster?".
+//
+// Two launches on the caller's stream:
+//
+//  stage_kernel  turns hidden*scale (exact in binary32) into a 24-bit
+//      fixed-point code per token (power-of-two step from the token's largest
+//      |hidden*scale|), splits each code into three signed bytes (limbs) and
+//      writes them to the workspace already laid out as MFMA A-operand
+//      fragments, together with each token's step exponent.
+//
+//  verify_kernel  streams the head once.  Persistent workgroups (one per CU)
+//      walk vocabulary tiles of 16 rows b, b+G, b+2G, ...  A tile (16 rows x
+//      H/2 bytes, contiguous in memory) is copied straight into an LDS ring
+//      with global_load_lds_dwordx4: each instruction moves 1 KB of
+//      consecutive bytes (whole cache lines, non-temporal), and the ring holds
+//      several tiles in flight without using registers.  The 16-byte chunks
+//      are XOR-swizzled inside each 1 KB block so that the fragment reads
+//      below hit distinct LDS banks.  The 8 waves split the hidden dimension;
+//      each keeps its slice of the activation limbs in registers for the whole
+//      call.  A weight nibble becomes the int8 value 16*q by moving it to the
+//      high half of a byte (two bit operations per 8 weights) and
+//      v_mfma_i32_16x16x64_i8 accumulates exactly in int32.  Each wave
+//      combines its limbs (weights 2^16, 2^8, 1) into int64 partial sums and
+//      stores them in LDS; after the next barrier the lanes that own a token
+//      add the 8 waves' partials -- integer addition, exact and independent of
+//      order -- and round the logit to binary32 once.  Each wave folds two
+//      tokens' logits into a running argmax.  The last
+//      workgroup to finish (atomic ticket) merges the per-workgroup winners,
+//      writes the outputs, counts accepted drafts and resets the ticket.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "int4vh.h"
+
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWaves = 8;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;     // 512
+constexpr int kTileRows = 16;             // vocabulary rows per tile (MFMA N)
+constexpr int kUnitH = 128;               // hidden channels per unit (16 rows x 64 B = 1 KB)
+constexpr int kMaxUnitsPerWave = 8;       // 8 waves x 8 units x 128 = 8192 channels
+constexpr int kMaxRows = 16;              // rows per launch (MFMA M)
+constexpr int kCodeMax = 8355711;         // |code| bound: all three limbs stay in int8
+constexpr int kMaxGrid = 1024;            // partial slots in the workspace
+constexpr int kStageSplit = 16;           // workgroups per token slot in stage_kernel
+
+// Workspace layout (bytes from the 256-byte aligned base).
+constexpr size_t kWsTicket = 0;                               // uint32 ticket
+constexpr size_t kWsExp = 64;                                 // int32 [16] step exponents
+constexpr size_t kWsPart = 256;                               // uint64 [kMaxGrid][16]
+constexpr size_t kWsFrag = kWsPart + (size_t)kMaxGrid * kMaxRows * 8;
+constexpr size_t kFragBytes = (size_t)kWaves * kMaxUnitsPerWave * 2 * 3 * 64 * 16;
+constexpr size_t kWsBytes = kWsFrag + kFragBytes;
+
+#ifndef INT4VH_WEIGHT_AUX
+#define INT4VH_WEIGHT_AUX 2                // cache policy of the weight stream: non-temporal
+#endif
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8).
+constexpr int waitcnt_vm(int n)
+{
+    return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8);
+}
+constexpr int kWaitLgkm0 = 0xF | (0x3 << 14) | (0x7 << 4);
+
+// Workgroup barrier without the release/acquire fences of __syncthreads (a
+// fence would also wait for the weight copies still in flight).  The caller
+// issues the s_waitcnt that its protocol needs; the empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void barrier_no_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// LDS writes of the partial sums go through inline asm: the compiler orders
+// every LDS write it can see after all LDS copies still in flight (a full
+// vmcnt(0) drain of the weight stream), although the partial sums and the
+// ring never overlap.  Completion of these writes is covered by the explicit
+// lgkmcnt(0) before each barrier.
+typedef __attribute__((address_space(3))) unsigned long long lds_u64;
+
+__device__ __forceinline__ uint32_t lds_offset(unsigned long long *p)
+{
+    return (uint32_t)(size_t)(lds_u64 *)p;
+}
+
+__device__ __forceinline__ void lds_store_u64(unsigned long long *p, unsigned long long v)
+{
+    asm volatile("ds_write_b64 %0, %1" ::"v"(lds_offset(p)), "v"(v) : "memory");
+}
+
+struct Args {
+    const uint16_t *hidden;   // [M, H] binary16
+    const uint8_t *w;         // [V, H/2]
+    const uint16_t *scales;   // [H]
+    const int32_t *draft;     // [R, T-1] or null
+    float *logits_max;        // [M]
+    int32_t *argmax;          // [M]
+    int32_t *n_acc;           // [R]
+    float *logits_out;        // [M, V] or null
+    uint64_t *part;           // [grid, M] packed (index << 32 | value bits)
+    uint32_t *ticket;
+    int32_t *exps;            // [16]
+    const u32x4 *frag;        // activation fragments
+    u32x4 *frag_out;
+    int R, T, M, V, H;
+    int n_units;              // ceil(H / 128)
+    int n_tiles;              // ceil(V / 16)
+    unsigned long long w_bytes;
+};
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t b)
+{
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// (value, index) order: larger value first, lower index on equal values.
+// -0.0 == +0.0 compare equal, so they tie and the lower index wins.
+__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
+{
+    return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+__device__ __forceinline__ uint64_t pack_pair(float v, int i)
+{
+    return ((uint64_t)(uint32_t)i << 32) | (uint64_t)__float_as_uint(v);
+}
+
+// 16 consecutive hidden*scale products (binary32, exact) of one row.
+__device__ __forceinline__ void load_xs16(const uint16_t *hrow, const uint16_t *scales, int h0,
+                                          float (&xs)[16])
+{
+    const u32x4 *hp = reinterpret_cast<const u32x4 *>(hrow + h0);
+    const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + h0);
+    u32x4 hx[2] = {hp[0], hp[1]};
+    u32x4 sx[2] = {sp[0], sp[1]};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        uint32_t hw = hx[j >> 3][(j >> 1) & 3], sw = sx[j >> 3][(j >> 1) & 3];
+        uint32_t hb = (j & 1) ? (hw >> 16) : (hw & 0xFFFF);
+        uint32_t sb = (j & 1) ? (sw >> 16) : (sw & 0xFFFF);
+        xs[j] = half_bits_to_float(hb) * half_bits_to_float(sb);
+    }
+}
+
+// Slot order of one K-step fragment (4 registers x 4 bytes), matching the
+// weight dequantisation below: register v, byte b holds hidden offset
+// 8*(v>>1) + 2*b + (v&1) within the 16 channels of the fragment.
+__device__ __forceinline__ int frag_offset(int v, int b)
+{
+    return 8 * (v >> 1) + 2 * b + (v & 1);
+}
+
+// Rows of the 16-row MFMA operand A are (token, limb) slots: slot s of group
+// g (s = 16*g + row) holds limb s / kP of token s % kP, so every lane carries
+// one token (row % kP) and the three limbs of all tokens need
+// ceil(3*kP / 16) MFMAs per K-step: kP = 5 (<= 5 rows, 1 MFMA), 8 (<= 8
+// rows, 2 MFMAs) or 16 (<= 16 rows, 3 MFMAs).
+template <int kP>
+struct Slots {
+    static constexpr int kGroups = (3 * kP + 15) / 16;
+};
+
+// Index of the fragment (wave, unit i, K-step t, group g, lane) in the workspace.
+template <int kP, int kUnits>
+__device__ __forceinline__ size_t frag_index(int wave, int i, int t, int g, int lane)
+{
+    return ((((size_t)wave * kUnits + i) * 2 + t) * Slots<kP>::kGroups + g) * 64 + lane;
+}
+
+// Smallest e with amax / 2^e <= kCodeMax (0 for amax == 0).
+__device__ __forceinline__ int code_exponent(float amax)
+{
+    if (!(amax > 0.0f))
+        return 0;
+    int ex;
+    frexpf(amax, &ex);                    // amax = f * 2^ex, f in [0.5, 1)
+    int e = ex - 23;                      // amax / 2^e in [2^22, 2^23)
+    if (ldexpf(amax, -e) > (float)kCodeMax)
+        ++e;
+    return e;
+}
+
+// ---------------------------------------------------------------- stage_kernel
+// Grid: kP token slots x kStageSplit.  Every workgroup of slot tau recomputes
+// tau's step exponent (a cheap reduction over H) and writes its share of
+// tau's fragments; slots tau >= M, and rows whose limb index is 3, get zeros.
+template <int kP, int kUnits>
+__global__ void __launch_bounds__(256) stage_kernel(Args a)
+{
+    constexpr int kGroups = Slots<kP>::kGroups;
+    __shared__ float s_red[4];
+    const int tau = blockIdx.x / kStageSplit;
+    const int split = blockIdx.x % kStageSplit;
+    const int H = a.H;
+    const bool live = tau < a.M;
+    const uint16_t *hrow = a.hidden + (size_t)(live ? tau : 0) * H;
+
+    // largest |hidden*scale| of the token: 8 channels per 16-byte load, all
+    // loads in flight together
+    float am = 0.0f;
+    if (live) {
+        constexpr int kIter = (INT4VH_MAX_H / 8 + 255) / 256;
+        const u32x4 *hv = reinterpret_cast<const u32x4 *>(hrow);
+        const u32x4 *sv = reinterpret_cast<const u32x4 *>(a.scales);
+        const int nv = H / 8;
+        u32x4 xq[kIter], sq[kIter];
+#pragma unroll
+        for (int it = 0; it < kIter; ++it) {
+            const int i = threadIdx.x + 256 * it;
+            xq[it] = i < nv ? hv[i] : u32x4{0u, 0u, 0u, 0u};
+            sq[it] = i < nv ? sv[i] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < kIter; ++it)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t hb = (j & 1) ? (xq[it][j >> 1] >> 16) : (xq[it][j >> 1] & 0xFFFF);
+                const uint32_t sb = (j & 1) ? (sq[it][j >> 1] >> 16) : (sq[it][j >> 1] & 0xFFFF);
+                am = fmaxf(am, fabsf(half_bits_to_float(hb) * half_bits_to_float(sb)));
+            }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        am = fmaxf(am, __shfl_xor(am, off));
+    if ((threadIdx.x & 63) == 0)
+        s_red[threadIdx.x >> 6] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    const int e = code_exponent(am);
+    if (split == 0 && threadIdx.x == 0)
+        a.exps[tau] = e;
+
+    // fragments owned by tau: lanes whose row n16 satisfies n16 % kP == tau
+    const int n_rows = (16 - tau + kP - 1) / kP;          // such rows n16 = tau + kP*j
+    const int per_chunk = n_rows * 4;                     // x 4 lane groups
+    const int total = kWaves * kUnits * 2 * kGroups * per_chunk;
+    for (int idx = split * 256 + threadIdx.x; idx < total; idx += kStageSplit * 256) {
+        int r = idx;
+        const int grp = r % 4;
+        r /= 4;
+        const int jrow = r % n_rows;
+        r /= n_rows;
+        const int g = r % kGroups;
+        r /= kGroups;
+        const int t = r % 2;
+        r /= 2;
+        const int i = r % kUnits;
+        const int wave = r / kUnits;
+        const int n16 = tau + kP * jrow;
+        const int limb = (16 * g + n16) / kP;
+        const int u = wave * kUnits + i;
+        const int h0 = u * kUnitH + grp * 32 + t * 16;
+        u32x4 word = {0u, 0u, 0u, 0u};
+        if (live && limb < 3 && u < a.n_units && h0 < H) {
+            float xs[16];
+            load_xs16(hrow, a.scales, h0, xs);
+            int8_t lb[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int c = (int)rintf(ldexpf(xs[j], -e));
+                const int lo = (int)(int8_t)(c & 0xFF);
+                const int c1 = (c - lo) >> 8;
+                const int mid = (int)(int8_t)(c1 & 0xFF);
+                const int hi = (c1 - mid) >> 8;
+                lb[j] = (int8_t)(limb == 0 ? hi : limb == 1 ? mid : lo);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                uint32_t wd = 0;
+#pragma unroll
+                for (int bb = 0; bb < 4; ++bb)
+                    wd |= (uint32_t)(uint8_t)lb[frag_offset(v, bb)] << (8 * bb);
+                word[v] = wd;
+            }
+        }
+        a.frag_out[frag_index<kP, kUnits>(wave, i, t, g, grp * 16 + n16)] = word;
+    }
+}
+
+// ---------------------------------------------------------------- verify_kernel
+template <int kP, int kUnits, int kRing, bool kLogits>
+__global__ void __launch_bounds__(kThreads)
+verify_kernel(Args a)
+{
+    constexpr int kGroups = Slots<kP>::kGroups;
+    constexpr int kTileBytes = kUnits * kWaves * 1024;     // LDS image of one tile (max H)
+    // All LDS lives in one object: the weight ring, then the per-wave
+    // partial sums (int64 per D row and column, two buffers).  The final
+    // merge reuses the ring once it is dead.
+    struct Merge {
+        float fv[32][kMaxRows];
+        int fi[32][kMaxRows];
+        int arg[kMaxRows];
+        int last;
+    };
+    struct Lds {
+        uint8_t ring[kRing][kTileBytes];
+        unsigned long long part[2][kWaves][kTileRows][kTileRows];
+    };
+    static_assert(sizeof(Merge) <= sizeof(uint8_t[kRing][kTileBytes]), "merge area");
+    static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) Lds lds;
+    auto &s_ring = lds.ring;
+    auto &s_part = lds.part;
+    Merge &mg = *reinterpret_cast<Merge *>(&lds.ring[0][0]);
+    auto &s_fv = mg.fv;
+    auto &s_fi = mg.fi;
+    auto &s_arg = mg.arg;
+    auto &s_last = mg.last;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n16 = lane & 15;   // MFMA row of A / column of B and D
+    const int grp = lane >> 4;   // 16-lane group: K sub-block, D rows 4*grp..4*grp+3
+    const int G = gridDim.x;
+    const int b = blockIdx.x;
+    const int M = a.M, V = a.V, H = a.H;
+    const int n_my = (a.n_tiles - b + G - 1) / G;
+    const int chunks_per_row = H / 32;                     // 16-byte chunks per weight row
+
+    // ---------------- activation fragments and step exponents (from stage_kernel)
+    i32x4 afr[kUnits][2][kGroups];
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                afr[i][t][g] = __builtin_bit_cast(i32x4, a.frag[frag_index<kP, kUnits>(wave, i, t, g, lane)]);
+    const int rtok = 2 * wave + ((lane >> 4) & 1);         // token reduced by this lane
+    const bool rlane = lane < 32 && rtok < M;
+    const int rexp = a.exps[rtok < M ? rtok : 0] - 4;      // weights carry a factor 16
+
+    // ---------------- weight stream into the LDS ring
+    // Wave w copies 1 KB blocks jj = w*kUnits + m of the tile (m < kUnits);
+    // lane l of a block fetches chunk l ^ (jj & 7) so that LDS holds the
+    // tile image with chunk c of block jj at position c ^ (jj & 7).  Blocks
+    // past the tile and bytes past the head are clamped (their values are
+    // never used: zero activation codes or masked rows), which keeps every
+    // wave's number of copies per tile fixed.
+    const unsigned long long w_last = a.w_bytes - 16;
+    auto issue_tile = [&](int k) {
+        const int tile = b + k * G;
+        const unsigned long long base = (unsigned long long)tile * kTileRows * (H / 2);
+        uint8_t *dst = s_ring[k % kRing];
+#pragma unroll
+        for (int m = 0; m < kUnits; ++m) {
+            const int jj = min(wave * kUnits + m, a.n_units - 1);
+            const unsigned long long off = base + (unsigned long long)jj * 1024 + (unsigned long long)((lane ^ (jj & 7)) * 16);
+            __builtin_amdgcn_global_load_lds(a.w + (off < w_last ? off : w_last),
+                                             (lds_void *)(dst + jj * 1024), 16, 0, INT4VH_WEIGHT_AUX);
+        }
+    };
+#pragma unroll
+    for (int k = 0; k < kRing - 1; ++k)
+        if (k < n_my)
+            issue_tile(k);
+
+    // LDS byte offsets of this lane's B fragments (swizzled), per unit
+    int boff[kUnits];
+#pragma unroll
+    for (int i = 0; i < kUnits; ++i) {
+        const int gc = n16 * chunks_per_row + (wave * kUnits + i) * 4 + grp;
+        const int jj = gc >> 6;
+        boff[i] = (jj * 64 + ((gc & 63) ^ (jj & 7))) * 16;
+    }
+    // limb weights (shift) and token of the four D rows this lane receives
+    int shift[kGroups][4];
+    int dtok[4];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+        const int row = grp * 4 + r4;
+        dtok[r4] = row % kP;
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g) {
+            const int l = (16 * g + row) / kP;
+            shift[g][r4] = l < 3 ? 8 * (2 - l) : -1;
+        }
+    }
+
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7FFFFFFF;
+    // Rows of D that hold limbs of token rtok: rtok, rtok + kP, ... (< 16).
+    auto reduce_tile = [&](int k) {
+        if (rlane) {
+            const int buf = k & 1;
+            long long code = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+                for (int r = 0; r < kTileRows; r += kP)
+                    if (rtok + r < kTileRows)
+                        code += (long long)s_part[buf][w][rtok + r][n16];
+            const int v = (b + k * G) * kTileRows + n16;
+            const float val = (float)ldexp((double)code, rexp);   // the one rounding
+            if (v < V) {
+                if (better(val, v, bv, bi)) {
+                    bv = val;
+                    bi = v;
+                }
+                if (kLogits)
+                    a.logits_out[(size_t)rtok * V + v] = val;
+            }
+        }
+    };
+
+    // ---------------- main loop over this workgroup's tiles
+    for (int k = 0; k < n_my; ++k) {
+        // this wave's copies of tile k are done (later tiles may be in flight);
+        // after the barrier every wave's copies are, and tile k-1's partial
+        // sums are complete in s_part
+        // copies issued after tile k's: min(kRing - 2, n_my - 1 - k) tiles
+        static_assert(kRing >= 2 && kRing <= 4, "ring depth");
+        const int later = min(kRing - 2, n_my - 1 - k);
+        if (later >= 2)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kUnits));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(kUnits));
+        else
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        barrier_no_fence();
+        if (k + kRing - 1 < n_my)
+            issue_tile(k + kRing - 1);
+
+        const uint8_t *tile = s_ring[k % kRing];
+        u32x4 q[kUnits];
+#pragma unroll
+        for (int i = 0; i < kUnits; ++i)
+            q[i] = *reinterpret_cast<const u32x4 *>(tile + boff[i]);
+        i32x4 acc[kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; ++g)
+            acc[g] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < kUnits; ++i) {
+            // nibble -> high half of a byte: the int8 value is 16*q
+            const i32x4 b0 = {(int32_t)((q[i][0] << 4) & 0xF0F0F0F0u), (int32_t)(q[i][0] & 0xF0F0F0F0u),
+                              (int32_t)((q[i][1] << 4) & 0xF0F0F0F0u), (int32_t)(q[i][1] & 0xF0F0F0F0u)};
+            const i32x4 b1 = {(int32_t)((q[i][2] << 4) & 0xF0F0F0F0u), (int32_t)(q[i][2] & 0xF0F0F0F0u),
+                              (int32_t)((q[i][3] << 4) & 0xF0F0F0F0u), (int32_t)(q[i][3] & 0xF0F0F0F0u)};
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(afr[i][0][g], b0, acc[g], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(afr[i][1][g], b1, acc[g], 0, 0, 0);
+        }
+
+        if (k > 0)
+            reduce_tile(k - 1);
+
+        // this wave's partial codes, limbs combined (exact int64), one per D row
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            long long val = 0;
+#pragma unroll
+            for (int g = 0; g < kGroups; ++g)
+                if (shift[g][r4] >= 0)
+                    val += (long long)acc[g][r4] << shift[g][r4];
+            if (dtok[r4] < M)
+                lds_store_u64(&s_part[k & 1][wave][grp * 4 + r4][n16], (unsigned long long)val);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    barrier_no_fence();
+    reduce_tile(n_my - 1);
+
+    // ---------------- per-workgroup best per token
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    // Publication without device-scope fences: a fence here writes back and
+    // invalidates the whole L2 of the XCD, which costs tens of microseconds
+    // when every workgroup does it.  The winners and the ticket are
+    // agent-scope atomics, which are coherent across XCDs by themselves; each
+    // wave waits until its store is acknowledged before the barrier, so every
+    // store has landed before the ticket is incremented, and the last
+    // workgroup reads them with agent-scope atomic loads.
+    if (rlane && n16 == 0)
+        __hip_atomic_store(&a.part[(size_t)b * M + rtok], pack_pair(bv, bi), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == (uint32_t)(G - 1));
+    }
+    __syncthreads();
+    if (!s_last)
+        return;
+
+    // ---------------- last workgroup: merge, write, accept, reset
+    {
+        const int m = threadIdx.x & 15;
+        const int slot = threadIdx.x >> 4;   // 0..31
+        float v0 = -__builtin_huge_valf();
+        int i0 = 0x7FFFFFFF;
+        if (m < M) {
+            // these loads bypass the non-coherent L2: issue them all before
+            // using any, so the merge costs one memory round trip
+            constexpr int kPerThread = kMaxGrid / 32;
+            uint64_t p[kPerThread];
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                const int bb = slot + 32 * j;
+                p[j] = bb < G ? __hip_atomic_load(&a.part[(size_t)bb * M + m], __ATOMIC_RELAXED,
+                                                  __HIP_MEMORY_SCOPE_AGENT)
+                              : pack_pair(-__builtin_huge_valf(), 0x7FFFFFFF);
+            }
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                const float pv = __uint_as_float((uint32_t)p[j]);
+                const int pi = (int)(uint32_t)(p[j] >> 32);
+                if (better(pv, pi, v0, i0)) {
+                    v0 = pv;
+                    i0 = pi;
+                }
+            }
+        }
+        s_fv[slot][m] = v0;
+        s_fi[slot][m] = i0;
+    }
+    __syncthreads();
+    if (threadIdx.x < (unsigned)M) {
+        const int m = threadIdx.x;
+        float v0 = s_fv[0][m];
+        int i0 = s_fi[0][m];
+        for (int sl = 1; sl < 32; ++sl)
+            if (better(s_fv[sl][m], s_fi[sl][m], v0, i0)) {
+                v0 = s_fv[sl][m];
+                i0 = s_fi[sl][m];
+            }
+        a.logits_max[m] = v0;
+        a.argmax[m] = i0;
+        s_arg[m] = i0;
+    }
+    __syncthreads();
+    if (threadIdx.x < (unsigned)a.R) {
+        const int req = threadIdx.x;
+        const int T = a.T;
+        int n = 0;
+        while (n < T - 1 && s_arg[req * T + n] == a.draft[(size_t)req * (T - 1) + n])
+            ++n;
+        a.n_acc[req] = n;
+    }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------- small kernels
+
+__global__ void fill_zero_u32(uint32_t *p, int n)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
+__global__ void __launch_bounds__(256) count_bad_nibbles(const u32x4 *w, size_t n_vec, int32_t *out)
+{
+    int cnt = 0;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vec;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const u32x4 q = __builtin_nontemporal_load(w + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // a nibble equals 0x8 iff (nib ^ 0x8) == 0
+            const uint32_t x = q[j] ^ 0x88888888u;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                cnt += ((x >> (4 * k)) & 0xFu) == 0u;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        cnt += __shfl_xor(cnt, off);
+    if ((threadIdx.x & 63) == 0 && cnt)
+        atomicAdd(out, cnt);
+}
+
+// ---------------------------------------------------------------- host side
+
+thread_local std::string g_last_error;
+
+int hip_fail(hipError_t e, const char *what)
+{
+    g_last_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+    return INT4VH_EHIP;
+}
+
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+
+int cu_count(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return 256;
+    std::call_once(g_cu_once[dev], [dev] {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_cu_count[dev] = n;
+    });
+    return g_cu_count[dev];
+}
+
+bool aligned(const void *p, size_t al)
+{
+    return ((uintptr_t)p % al) == 0;
+}
+
+typedef void (*KernelFn)(Args);
+
+struct Pair {
+    KernelFn stage;
+    KernelFn verify;
+};
+
+// Ring depth: three tiles in flight while they fit in LDS, else two.
+template <int kP, int kUnits, bool kLogits>
+Pair make_pair()
+{
+    constexpr int kRing = kUnits <= 5 ? 3 : 2;
+    return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits>};
+}
+
+template <int kP, bool kLogits>
+Pair pick(int units)
+{
+    switch (units) {
+    case 1: return make_pair<kP, 1, kLogits>();
+    case 2: return make_pair<kP, 2, kLogits>();
+    case 3: return make_pair<kP, 3, kLogits>();
+    case 4: return make_pair<kP, 4, kLogits>();
+    case 5: return make_pair<kP, 5, kLogits>();
+    case 6: return make_pair<kP, 6, kLogits>();
+    case 7: return make_pair<kP, 7, kLogits>();
+    default: return make_pair<kP, 8, kLogits>();
+    }
+}
+
+template <bool kLogits>
+Pair pick_rows(int M, int units, int *kp)
+{
+    if (M <= 5) {
+        *kp = 5;
+        return pick<5, kLogits>(units);
+    }
+    if (M <= 8) {
+        *kp = 8;
+        return pick<8, kLogits>(units);
+    }
+    *kp = 16;
+    return pick<16, kLogits>(units);
+}
+
+size_t workspace_need(int R, int T, int V, int H)
+{
+    if (R < 1 || T < 1 || T > INT4VH_MAX_T || V < 1 || H < 32 || (H % 32) != 0)
+        return 0;
+    if ((long long)R * T > kMaxRows)
+        return 0;
+    return kWsBytes;
+}
+
+int validate(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
+             int R, int T, int V, int H, const float *lmax, const int32_t *amax_ids,
+             const int32_t *nacc, const float *lout, const void *ws, size_t ws_bytes)
+{
+    if (R < 1 || T < 1 || T > INT4VH_MAX_T || V < 1 || H < 32 || (H % 32) != 0)
+        return INT4VH_EINVAL;
+    if ((long long)R * T > kMaxRows)
+        return INT4VH_EINVAL;
+    if (!hidden || !w || !scales || !lmax || !amax_ids || !nacc || !ws)
+        return INT4VH_EINVAL;
+    if (T > 1 && !draft)
+        return INT4VH_EINVAL;
+    if (H > INT4VH_MAX_H)
+        return INT4VH_EUNSUPPORTED;
+    if ((unsigned long long)V * (unsigned long long)(H / 2) >= (1ull << 40))
+        return INT4VH_EUNSUPPORTED;
+    if (!aligned(hidden, 16) || !aligned(w, 16) || !aligned(scales, 16) || !aligned(lmax, 16) ||
+        !aligned(amax_ids, 16) || !aligned(nacc, 4) || (draft && !aligned(draft, 4)) ||
+        (lout && !aligned(lout, 16)) || !aligned(ws, 256))
+        return INT4VH_EALIGN;
+    if (ws_bytes < workspace_need(R, T, V, H))
+        return INT4VH_EWORKSPACE;
+    return INT4VH_OK;
+}
+
+int launch_verify(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
+                  int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
+                  float *lout, void *ws, size_t ws_bytes, void *stream)
+{
+    const int st = validate(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, ws,
+                            ws_bytes);
+    if (st != INT4VH_OK)
+        return st;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+
+    char *wsb = static_cast<char *>(ws);
+    Args a;
+    a.hidden = static_cast<const uint16_t *>(hidden);
+    a.w = w;
+    a.scales = static_cast<const uint16_t *>(scales);
+    a.draft = draft;
+    a.logits_max = lmax;
+    a.argmax = amax_ids;
+    a.n_acc = nacc;
+    a.logits_out = lout;
+    a.ticket = reinterpret_cast<uint32_t *>(wsb + kWsTicket);
+    a.exps = reinterpret_cast<int32_t *>(wsb + kWsExp);
+    a.part = reinterpret_cast<uint64_t *>(wsb + kWsPart);
+    a.frag = reinterpret_cast<const u32x4 *>(wsb + kWsFrag);
+    a.frag_out = reinterpret_cast<u32x4 *>(wsb + kWsFrag);
+    a.R = R;
+    a.T = T;
+    a.M = R * T;
+    a.V = V;
+    a.H = H;
+    a.n_units = (H + kUnitH - 1) / kUnitH;
+    a.n_tiles = (V + kTileRows - 1) / kTileRows;
+    a.w_bytes = (unsigned long long)V * (unsigned long long)(H / 2);
+    const int units = (a.n_units + kWaves - 1) / kWaves;
+    int grid = cu_count(dev);
+    if (grid > kMaxGrid)
+        grid = kMaxGrid;
+    if (grid > a.n_tiles)
+        grid = a.n_tiles;
+    int kp = 16;
+    const Pair fn = lout ? pick_rows<true>(a.M, units, &kp) : pick_rows<false>(a.M, units, &kp);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(fn.stage, dim3(kp * kStageSplit), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "stage kernel launch");
+    hipLaunchKernelGGL(fn.verify, dim3(grid), dim3(kThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "verify kernel launch");
+    return INT4VH_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t verify_lm_head_int4_workspace_bytes(int R, int T, int V, int H)
+{
+    return workspace_need(R, T, V, H);
+}
+
+int verify_lm_head_int4_workspace_init(void *ws, size_t ws_bytes, void *stream)
+{
+    if (!ws)
+        return INT4VH_EINVAL;
+    if (!aligned(ws, 256))
+        return INT4VH_EALIGN;
+    if (ws_bytes < kWsPart)
+        return INT4VH_EWORKSPACE;
+    const int n = (int)(kWsPart / sizeof(uint32_t));
+    hipLaunchKernelGGL(fill_zero_u32, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<uint32_t *>(ws), n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "workspace init launch");
+    return INT4VH_OK;
+}
+
+int verify_lm_head_int4(const void *hidden, const uint8_t *packed_w, const void *scales,
+                        const int32_t *draft_ids, int T, int V, int H, float *logits_max,
+                        int32_t *argmax_ids, int32_t *n_accepted, float *logits_out,
+                        void *workspace, size_t workspace_bytes, void *stream)
+{
+    return launch_verify(hidden, packed_w, scales, draft_ids, 1, T, V, H, logits_max, argmax_ids,
+                         n_accepted, logits_out, workspace, workspace_bytes, stream);
+}
+
+int verify_lm_head_int4_batch(const void *hidden, const uint8_t *packed_w, const void *scales,
+                              const int32_t *draft_ids, int R, int T, int V, int H,
+                              float *logits_max, int32_t *argmax_ids, int32_t *n_accepted,
+                              float *logits_out, void *workspace, size_t workspace_bytes,
+                              void *stream)
+{
+    return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
+                         n_accepted, logits_out, workspace, workspace_bytes, stream);
+}
+
+int verify_lm_head_int4_check_weights(const uint8_t *packed_w, int V, int H, int32_t *n_bad_out,
+                                      void *stream)
+{
+    if (!packed_w || !n_bad_out || V < 1 || H < 32 || (H % 32) != 0)
+        return INT4VH_EINVAL;
+    if (!aligned(packed_w, 16) || !aligned(n_bad_out, 4))
+        return INT4VH_EALIGN;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(fill_zero_u32, dim3(1), dim3(64), 0, s, reinterpret_cast<uint32_t *>(n_bad_out), 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "check_weights zero launch");
+    const size_t n_vec = (size_t)V * (size_t)(H / 2) / 16;
+    size_t blocks = (n_vec + 255) / 256;
+    if (blocks > 4096)
+        blocks = 4096;
+    hipLaunchKernelGGL(count_bad_nibbles, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const u32x4 *>(packed_w), n_vec, n_bad_out);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "check_weights launch");
+    return INT4VH_OK;
+}
+
+const char *verify_lm_head_int4_status_string(int status)
+{
+    switch (status) {
+    case INT4VH_OK: return "ok";
+    case INT4VH_EINVAL: return "invalid argument";
+    case INT4VH_EALIGN: return "misaligned pointer";
+    case INT4VH_EWORKSPACE: return "workspace too small";
+    case INT4VH_EHIP: return "HIP runtime error";
+    case INT4VH_EUNSUPPORTED: return "unsupported shape";
+    default: return "unknown status";
+    }
+}
+
+const char *verify_lm_head_int4_last_error(void)
+{
+    return g_last_error.c_str();
+}
+
+} // extern "C"

@@ -1,0 +1,114 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects invalid arguments on the host before any GPU
+call (fake, never-dereferenced pointer values are used)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "int4vh.h")
+LIB = os.path.join(ROOT, "int4_output_head_amd", "libint4vh.so")
+
+OK, EINVAL, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(verify_lm_head_int4\w*)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from int4_output_head_amd.build import build_library
+        build_library()
+    L = ctypes.CDLL(LIB)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.verify_lm_head_int4.argtypes = [P, P, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.verify_lm_head_int4_batch.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+    L.verify_lm_head_int4_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.verify_lm_head_int4_workspace_bytes.restype = sz
+    L.verify_lm_head_int4_workspace_init.argtypes = [P, sz, P]
+    L.verify_lm_head_int4_check_weights.argtypes = [P, i32, i32, P, P]
+    L.verify_lm_head_int4_status_string.argtypes = [i32]
+    L.verify_lm_head_int4_status_string.restype = ctypes.c_char_p
+    L.verify_lm_head_int4_last_error.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_expected_api():
+    names = declared_functions()
+    assert "verify_lm_head_int4" in names and "verify_lm_head_int4_batch" in names
+    assert len(names) >= 7
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (OK, EINVAL, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED):
+        s = lib.verify_lm_head_int4_status_string(st)
+        assert s and s != b"unknown status"
+    assert lib.verify_lm_head_int4_status_string(12345) == b"unknown status"
+    assert lib.verify_lm_head_int4_last_error() == b""
+
+
+def test_workspace_bytes(lib):
+    n = lib.verify_lm_head_int4_workspace_bytes(1, 16, 151936, 5120)
+    assert n > 0 and n % 256 == 0
+    assert lib.verify_lm_head_int4_workspace_bytes(1, 0, 10, 64) == 0
+    assert lib.verify_lm_head_int4_workspace_bytes(1, 17, 10, 64) == 0
+    assert lib.verify_lm_head_int4_workspace_bytes(1, 4, 0, 64) == 0
+    assert lib.verify_lm_head_int4_workspace_bytes(1, 4, 10, 48) == 0
+
+
+A = 0x10000          # a fake, 256-byte aligned "device pointer" (never dereferenced)
+WS = 1 << 20
+
+
+def call(lib, hidden=A, w=A, s=A, d=A, T=4, V=100, H=256, lmax=A, amax=A, nacc=A, lout=None,
+         ws=A, ws_bytes=WS):
+    P = ctypes.c_void_p
+    return lib.verify_lm_head_int4(P(hidden), P(w), P(s), P(d), T, V, H, P(lmax), P(amax),
+                                   P(nacc), P(lout), P(ws), ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), EINVAL), (dict(T=17), EINVAL), (dict(V=0), EINVAL), (dict(H=16), EINVAL),
+    (dict(H=48), EINVAL), (dict(H=8224), EUNSUPPORTED), (dict(hidden=0), EINVAL),
+    (dict(w=0), EINVAL), (dict(s=0), EINVAL), (dict(d=0), EINVAL), (dict(lmax=0), EINVAL),
+    (dict(amax=0), EINVAL), (dict(nacc=0), EINVAL), (dict(ws=0), EINVAL),
+    (dict(hidden=A + 8), EALIGN), (dict(w=A + 4), EALIGN), (dict(s=A + 2), EALIGN),
+    (dict(lmax=A + 4), EALIGN), (dict(lout=A + 8), EALIGN), (dict(ws=A + 16), EALIGN),
+    (dict(d=A + 2), EALIGN), (dict(ws_bytes=100), EWORKSPACE),
+    (dict(V=1 << 30, H=4096), EUNSUPPORTED),
+])
+def test_verify_rejects_invalid_arguments(lib, kw, status):
+    assert call(lib, **kw) == status
+
+
+def test_draft_may_be_null_only_for_T1(lib):
+    assert call(lib, d=0, T=2) == EINVAL
+    assert call(lib, d=0, T=1, ws=A + 16) == EALIGN   # passes the draft check, fails later
+
+
+def test_batch_rejects_invalid(lib):
+    P = ctypes.c_void_p
+    f = lib.verify_lm_head_int4_batch
+    assert f(P(A), P(A), P(A), P(A), 0, 4, 10, 64, P(A), P(A), P(A), None, P(A), WS, None) == EINVAL
+    assert f(P(A), P(A), P(A), P(A), 5, 4, 10, 64, P(A), P(A), P(A), None, P(A), WS, None) == EINVAL
+
+
+def test_workspace_init_and_check_weights_validation(lib):
+    P = ctypes.c_void_p
+    assert lib.verify_lm_head_int4_workspace_init(None, WS, None) == EINVAL
+    assert lib.verify_lm_head_int4_workspace_init(P(A + 64), WS, None) == EALIGN
+    assert lib.verify_lm_head_int4_workspace_init(P(A), 16, None) == EWORKSPACE
+    assert lib.verify_lm_head_int4_check_weights(None, 10, 64, P(A), None) == EINVAL
+    assert lib.verify_lm_head_int4_check_weights(P(A), 10, 48, P(A), None) == EINVAL
+    assert lib.verify_lm_head_int4_check_weights(P(A + 8), 10, 64, P(A), None) == EALIGN
