@@ -67,6 +67,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="head copies to rotate (0: auto)")
     ap.add_argument("--cpu-trials", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain device copy of head-sized buffers (a known "
+                         "number of bytes) to scale hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -108,6 +111,16 @@ def main():
             ds.append(None)
     if stored is None:
         log("no stored oracle argmax for this config: drafts are not aligned with the target")
+
+    if args.calibrate_copy:
+        src = torch.empty(cfg.weight_bytes, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration: 3 device copies of {cfg.weight_bytes} bytes")
+        del src, dst
 
     work = binding.Workspace(binding.workspace_bytes(cfg.R, cfg.T, cfg.V, cfg.H), dev)
     stream = torch.cuda.current_stream(dev)
