@@ -143,9 +143,17 @@ def main():
     torch.cuda.synchronize()
     log(f"parity gate vs stored oracle argmax: {gate}")
 
-    for i in range(args.warmup):
+    # warm-up: at least --warmup calls and at least half a second of work (the
+    # first calls after start read low until clocks settle)
+    t_w = time.time()
+    i = 0
+    while i < args.warmup or time.time() - t_w < 0.5:
         step(i)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    log(f"warm-up: {i} calls")
 
     # (1) eager launches, one HIP event pair around each call: the per-launch
     #     duration of the C-ABI call (both of its kernels) for the roofline

@@ -62,7 +62,7 @@ constexpr int kMaxUnitsPerWave = 8;       // 8 waves x 8 units x 128 = 8192 chan
 constexpr int kMaxRows = 16;              // rows per launch (MFMA M)
 constexpr int kCodeMax = 8355711;         // |code| bound: all three limbs stay in int8
 constexpr int kMaxGrid = 1024;            // partial slots in the workspace
-constexpr int kStageSplit = 16;           // workgroups per token slot in stage_kernel
+constexpr int kStageThreads = 512;        // threads of stage_kernel (one 16-channel chunk each)
 
 // Workspace layout (bytes from the 256-byte aligned base).
 constexpr size_t kWsTicket = 0;                               // uint32 ticket
@@ -205,43 +205,40 @@ __device__ __forceinline__ int code_exponent(float amax)
 }
 
 // ---------------------------------------------------------------- stage_kernel
-// Grid: kP token slots x kStageSplit.  Every workgroup of slot tau recomputes
-// tau's step exponent (a cheap reduction over H) and writes its share of
-// tau's fragments; slots tau >= M, and rows whose limb index is 3, get zeros.
+// One workgroup per token slot tau < kP.  Thread c owns the 16-channel chunk
+// c of the token's row: it loads x and s for its chunk once, the block finds
+// the token's largest |x*s|, and the thread turns its 16 products into codes
+// and writes every fragment word that holds this chunk (one per lane row
+// n16 = tau, tau + kP, ... and lane group).  Slots tau >= M, and rows whose
+// limb index is 3, get zeros.
 template <int kP, int kUnits>
-__global__ void __launch_bounds__(256) stage_kernel(Args a)
+__global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
 {
     constexpr int kGroups = Slots<kP>::kGroups;
-    __shared__ float s_red[4];
-    const int tau = blockIdx.x / kStageSplit;
-    const int split = blockIdx.x % kStageSplit;
+    __shared__ float s_red[kStageThreads / 64];
+    const int tau = blockIdx.x;
     const int H = a.H;
     const bool live = tau < a.M;
     const uint16_t *hrow = a.hidden + (size_t)(live ? tau : 0) * H;
+    const int n_chunks = kWaves * kUnits * 8;              // 16-channel chunks in the padded row
+    constexpr int kIter = (kWaves * kMaxUnitsPerWave * 8 + kStageThreads - 1) / kStageThreads;
 
-    // largest |hidden*scale| of the token: 8 channels per 16-byte load, all
-    // loads in flight together
+    float xs[kIter][16];
     float am = 0.0f;
-    if (live) {
-        constexpr int kIter = (INT4VH_MAX_H / 8 + 255) / 256;
-        const u32x4 *hv = reinterpret_cast<const u32x4 *>(hrow);
-        const u32x4 *sv = reinterpret_cast<const u32x4 *>(a.scales);
-        const int nv = H / 8;
-        u32x4 xq[kIter], sq[kIter];
 #pragma unroll
-        for (int it = 0; it < kIter; ++it) {
-            const int i = threadIdx.x + 256 * it;
-            xq[it] = i < nv ? hv[i] : u32x4{0u, 0u, 0u, 0u};
-            sq[it] = i < nv ? sv[i] : u32x4{0u, 0u, 0u, 0u};
+    for (int it = 0; it < kIter; ++it) {
+        const int c = threadIdx.x + kStageThreads * it;
+        const bool ok = live && c < n_chunks && c * 16 < H;
+        if (ok) {
+            load_xs16(hrow, a.scales, c * 16, xs[it]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                xs[it][j] = 0.0f;
         }
 #pragma unroll
-        for (int it = 0; it < kIter; ++it)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t hb = (j & 1) ? (xq[it][j >> 1] >> 16) : (xq[it][j >> 1] & 0xFFFF);
-                const uint32_t sb = (j & 1) ? (sq[it][j >> 1] >> 16) : (sq[it][j >> 1] & 0xFFFF);
-                am = fmaxf(am, fabsf(half_bits_to_float(hb) * half_bits_to_float(sb)));
-            }
+        for (int j = 0; j < 16; ++j)
+            am = fmaxf(am, fabsf(xs[it][j]));
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
@@ -249,55 +246,52 @@ __global__ void __launch_bounds__(256) stage_kernel(Args a)
     if ((threadIdx.x & 63) == 0)
         s_red[threadIdx.x >> 6] = am;
     __syncthreads();
-    am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    am = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kStageThreads / 64; ++w)
+        am = fmaxf(am, s_red[w]);
     const int e = code_exponent(am);
-    if (split == 0 && threadIdx.x == 0)
+    if (threadIdx.x == 0)
         a.exps[tau] = e;
 
-    // fragments owned by tau: lanes whose row n16 satisfies n16 % kP == tau
-    const int n_rows = (16 - tau + kP - 1) / kP;          // such rows n16 = tau + kP*j
-    const int per_chunk = n_rows * 4;                     // x 4 lane groups
-    const int total = kWaves * kUnits * 2 * kGroups * per_chunk;
-    for (int idx = split * 256 + threadIdx.x; idx < total; idx += kStageSplit * 256) {
-        int r = idx;
-        const int grp = r % 4;
-        r /= 4;
-        const int jrow = r % n_rows;
-        r /= n_rows;
-        const int g = r % kGroups;
-        r /= kGroups;
-        const int t = r % 2;
-        r /= 2;
-        const int i = r % kUnits;
-        const int wave = r / kUnits;
-        const int n16 = tau + kP * jrow;
-        const int limb = (16 * g + n16) / kP;
-        const int u = wave * kUnits + i;
-        const int h0 = u * kUnitH + grp * 32 + t * 16;
-        u32x4 word = {0u, 0u, 0u, 0u};
-        if (live && limb < 3 && u < a.n_units && h0 < H) {
-            float xs[16];
-            load_xs16(hrow, a.scales, h0, xs);
-            int8_t lb[16];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int c = (int)rintf(ldexpf(xs[j], -e));
-                const int lo = (int)(int8_t)(c & 0xFF);
-                const int c1 = (c - lo) >> 8;
+    for (int it = 0; it < kIter; ++it) {
+        const int c = threadIdx.x + kStageThreads * it;
+        if (c >= n_chunks)
+            break;
+        // chunk c = channels 16c..16c+15: unit u = c / 8, lane group grp =
+        // (c % 8) / 2, K-step t = c % 2; unit u belongs to wave u / kUnits
+        const int u = c / 8, grp = (c % 8) / 2, t = c % 2;
+        const int wave = u / kUnits, i = u % kUnits;
+        uint32_t limbw[3][4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            uint32_t w0 = 0, w1 = 0, w2 = 0;
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const int cval = (int)rintf(ldexpf(xs[it][frag_offset(v, bb)], -e));
+                const int lo = (int)(int8_t)(cval & 0xFF);
+                const int c1 = (cval - lo) >> 8;
                 const int mid = (int)(int8_t)(c1 & 0xFF);
                 const int hi = (c1 - mid) >> 8;
-                lb[j] = (int8_t)(limb == 0 ? hi : limb == 1 ? mid : lo);
+                w0 |= (uint32_t)(uint8_t)hi << (8 * bb);
+                w1 |= (uint32_t)(uint8_t)mid << (8 * bb);
+                w2 |= (uint32_t)(uint8_t)lo << (8 * bb);
             }
+            limbw[0][v] = w0;
+            limbw[1][v] = w1;
+            limbw[2][v] = w2;
+        }
+        for (int n16 = tau; n16 < 16; n16 += kP) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                uint32_t wd = 0;
-#pragma unroll
-                for (int bb = 0; bb < 4; ++bb)
-                    wd |= (uint32_t)(uint8_t)lb[frag_offset(v, bb)] << (8 * bb);
-                word[v] = wd;
+            for (int g = 0; g < kGroups; ++g) {
+                const int limb = (16 * g + n16) / kP;
+                u32x4 word = {0u, 0u, 0u, 0u};
+                if (limb < 3)
+                    word = u32x4{limbw[limb][0], limbw[limb][1], limbw[limb][2], limbw[limb][3]};
+                a.frag_out[frag_index<kP, kUnits>(wave, i, t, g, grp * 16 + n16)] = word;
             }
         }
-        a.frag_out[frag_index<kP, kUnits>(wave, i, t, g, grp * 16 + n16)] = word;
     }
 }
 
@@ -388,13 +382,11 @@ verify_kernel(Args a)
         const int jj = gc >> 6;
         boff[i] = (jj * 64 + ((gc & 63) ^ (jj & 7))) * 16;
     }
-    // limb weights (shift) and token of the four D rows this lane receives
+    // limb weight (shift) of each group's D rows this lane receives
     int shift[kGroups][4];
-    int dtok[4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
         const int row = grp * 4 + r4;
-        dtok[r4] = row % kP;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
             const int l = (16 * g + row) / kP;
@@ -404,17 +396,20 @@ verify_kernel(Args a)
 
     float bv = -__builtin_huge_valf();
     int bi = 0x7FFFFFFF;
-    // Rows of D that hold limbs of token rtok: rtok, rtok + kP, ... (< 16).
+    // Rows of D that hold limbs of token t are t, t + kP, t + 2*kP (those
+    // with a limb index below 3).  Every lane loads (clamped to a valid
+    // token) so the loads are straight-line and all in flight together.
+    constexpr int kRowsPerTok = (16 + kP - 1) / kP < 3 ? (16 + kP - 1) / kP : 3;
+    const int rt = rlane ? rtok : 0;
     auto reduce_tile = [&](int k) {
-        if (rlane) {
-            const int buf = k & 1;
-            long long code = 0;
+        const int buf = k & 1;
+        long long code = 0;
+#pragma unroll
+        for (int j = 0; j < kRowsPerTok; ++j)
 #pragma unroll
             for (int w = 0; w < kWaves; ++w)
-#pragma unroll
-                for (int r = 0; r < kTileRows; r += kP)
-                    if (rtok + r < kTileRows)
-                        code += (long long)s_part[buf][w][rtok + r][n16];
+                code += (long long)s_part[buf][w][rt + kP * j][n16];
+        if (rlane) {
             const int v = (b + k * G) * kTileRows + n16;
             const float val = (float)ldexp((double)code, rexp);   // the one rounding
             if (v < V) {
@@ -482,8 +477,8 @@ verify_kernel(Args a)
             for (int g = 0; g < kGroups; ++g)
                 if (shift[g][r4] >= 0)
                     val += (long long)acc[g][r4] << shift[g][r4];
-            if (dtok[r4] < M)
-                lds_store_u64(&s_part[k & 1][wave][grp * 4 + r4][n16], (unsigned long long)val);
+            // rows of tokens >= M hold zero activation codes, so val is 0
+            lds_store_u64(&s_part[k & 1][wave][grp * 4 + r4][n16], (unsigned long long)val);
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -766,7 +761,7 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     int kp = 16;
     const Pair fn = lout ? pick_rows<true>(a.M, units, &kp) : pick_rows<false>(a.M, units, &kp);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    hipLaunchKernelGGL(fn.stage, dim3(kp * kStageSplit), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(fn.stage, dim3(kp), dim3(kStageThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "stage kernel launch");
