@@ -306,9 +306,10 @@ verify_kernel(Args a)
     // partial sums (int64 per D row and column, two buffers).  The final
     // merge reuses the ring once it is dead.
     struct Merge {
-        float fv[32][kMaxRows];
-        int fi[32][kMaxRows];
+        float fv[kWaves][kMaxRows];
+        int fi[kWaves][kMaxRows];
         int arg[kMaxRows];
+        int draft[kMaxRows];
         int last;
     };
     struct Lds {
@@ -324,6 +325,7 @@ verify_kernel(Args a)
     auto &s_fv = mg.fv;
     auto &s_fi = mg.fi;
     auto &s_arg = mg.arg;
+    auto &s_draft = mg.draft;
     auto &s_last = mg.last;
 
     const int lane = threadIdx.x & 63;
@@ -517,25 +519,34 @@ verify_kernel(Args a)
         return;
 
     // ---------------- last workgroup: merge, write, accept, reset
+    // One memory round trip: every load below is issued before any is used.
+    // Thread (slot, m) takes the winners of workgroups slot, slot+32, ... for
+    // token m (agent-scope loads: the lines may be stale in this XCD's L2);
+    // the threads below R*(T-1) also fetch one draft id each.
     {
         const int m = threadIdx.x & 15;
         const int slot = threadIdx.x >> 4;   // 0..31
+        const int mm = m < M ? m : M - 1;    // rows past M repeat a real one (never written out)
+        const int n_draft = a.R * (a.T - 1);
+        const int dft = (int)threadIdx.x < n_draft ? a.draft[threadIdx.x] : 0;
         float v0 = -__builtin_huge_valf();
         int i0 = 0x7FFFFFFF;
-        if (m < M) {
-            // these loads bypass the non-coherent L2: issue them all before
-            // using any, so the merge costs one memory round trip
-            constexpr int kPerThread = kMaxGrid / 32;
-            uint64_t p[kPerThread];
+        constexpr int kPerThread = kMaxGrid / 32;
+        constexpr int kBatch = 8;
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j) {
-                const int bb = slot + 32 * j;
-                p[j] = bb < G ? __hip_atomic_load(&a.part[(size_t)bb * M + m], __ATOMIC_RELAXED,
-                                                  __HIP_MEMORY_SCOPE_AGENT)
-                              : pack_pair(-__builtin_huge_valf(), 0x7FFFFFFF);
+        for (int j0 = 0; j0 < kPerThread; j0 += kBatch) {
+            if (32 * j0 >= G)
+                break;
+            uint64_t p[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                int bb = slot + 32 * (j0 + j);
+                bb = bb < G ? bb : G - 1;    // repeats are harmless for a maximum
+                p[j] = __hip_atomic_load(&a.part[(size_t)bb * M + mm], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
             }
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j) {
+            for (int j = 0; j < kBatch; ++j) {
                 const float pv = __uint_as_float((uint32_t)p[j]);
                 const int pi = (int)(uint32_t)(p[j] >> 32);
                 if (better(pv, pi, v0, i0)) {
@@ -544,18 +555,41 @@ verify_kernel(Args a)
                 }
             }
         }
-        s_fv[slot][m] = v0;
-        s_fi[slot][m] = i0;
+        // the four slots of this wave (lanes m, m+16, m+32, m+48)
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            const float ov = __shfl_xor(v0, off);
+            const int oi = __shfl_xor(i0, off);
+            if (better(ov, oi, v0, i0)) {
+                v0 = ov;
+                i0 = oi;
+            }
+        }
+        const int wv = threadIdx.x >> 6;
+        if ((threadIdx.x & 63) < 16) {
+            s_fv[wv][m] = v0;
+            s_fi[wv][m] = i0;
+        }
+        if ((int)threadIdx.x < n_draft)
+            s_draft[threadIdx.x] = dft;
     }
     __syncthreads();
     if (threadIdx.x < (unsigned)M) {
         const int m = threadIdx.x;
-        float v0 = s_fv[0][m];
-        int i0 = s_fi[0][m];
-        for (int sl = 1; sl < 32; ++sl)
-            if (better(s_fv[sl][m], s_fi[sl][m], v0, i0)) {
-                v0 = s_fv[sl][m];
-                i0 = s_fi[sl][m];
+        float fv[kWaves];
+        int fi[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            fv[w] = s_fv[w][m];
+            fi[w] = s_fi[w][m];
+        }
+        float v0 = fv[0];
+        int i0 = fi[0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w)
+            if (better(fv[w], fi[w], v0, i0)) {
+                v0 = fv[w];
+                i0 = fi[w];
             }
         a.logits_max[m] = v0;
         a.argmax[m] = i0;
@@ -566,7 +600,7 @@ verify_kernel(Args a)
         const int req = threadIdx.x;
         const int T = a.T;
         int n = 0;
-        while (n < T - 1 && s_arg[req * T + n] == a.draft[(size_t)req * (T - 1) + n])
+        while (n < T - 1 && s_arg[req * T + n] == s_draft[req * (T - 1) + n])
             ++n;
         a.n_acc[req] = n;
     }
