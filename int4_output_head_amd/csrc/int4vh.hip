@@ -64,13 +64,21 @@ constexpr int kCodeMax = 8355711;         // |code| bound: all three limbs stay 
 constexpr int kMaxGrid = 1024;            // partial slots in the workspace
 constexpr int kStageThreads = 512;        // threads of stage_kernel (one 16-channel chunk each)
 
-// Workspace layout (bytes from the 256-byte aligned base).
-constexpr size_t kWsTicket = 0;                               // uint32 ticket
-constexpr size_t kWsExp = 64;                                 // int32 [16] step exponents
-constexpr size_t kWsPart = 256;                               // uint64 [kMaxGrid][16]
-constexpr size_t kWsFrag = kWsPart + (size_t)kMaxGrid * kMaxRows * 8;
+constexpr int kBatchMaxRows = 4096;       // rows per launch of the batch path
+
+// Workspace layout (bytes from the 256-byte aligned base).  The control block
+// (ticket and per-row keys) is zeroed by workspace_init and left zeroed by
+// every call; the rest is written before it is read.
+constexpr size_t kWsTicket = 0;                                   // uint32 ticket
+constexpr size_t kWsKeys = 256;                                   // uint64 [4096] batch winner keys
+constexpr size_t kWsCtlBytes = kWsKeys + (size_t)kBatchMaxRows * 8;
+constexpr size_t kWsExp = kWsCtlBytes;                            // int32 [4096] step exponents
+constexpr size_t kWsPart = kWsExp + (size_t)kBatchMaxRows * 4;    // uint64 [kMaxGrid][16]
+constexpr size_t kWsFrag = kWsPart + (size_t)kMaxGrid * kMaxRows * 8;   // activation fragments
 constexpr size_t kFragBytes = (size_t)kWaves * kMaxUnitsPerWave * 2 * 3 * 64 * 16;
 constexpr size_t kWsBytes = kWsFrag + kFragBytes;
+static_assert(kWsCtlBytes % 256 == 0 && kWsExp % 256 == 0 && kWsPart % 256 == 0 &&
+                  kWsFrag % 256 == 0, "workspace regions stay 256-byte aligned");
 
 #ifndef INT4VH_WEIGHT_AUX
 #define INT4VH_WEIGHT_AUX 2                // cache policy of the weight stream: non-temporal
@@ -204,6 +212,32 @@ __device__ __forceinline__ int code_exponent(float amax)
     return e;
 }
 
+// Codes of 16 products (step 2^e, round to nearest even) split into three
+// signed bytes, high limb first (code = 2^16*l0 + 2^8*l1 + l2), packed in
+// fragment slot order: limbw[l][v] byte b holds limb l of the product at
+// frag_offset(v, b).
+__device__ __forceinline__ void split_limbs(const float (&xs)[16], int e, uint32_t (&limbw)[3][4])
+{
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        uint32_t w0 = 0, w1 = 0, w2 = 0;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const int cval = (int)rintf(ldexpf(xs[frag_offset(v, bb)], -e));
+            const int lo = (int)(int8_t)(cval & 0xFF);
+            const int c1 = (cval - lo) >> 8;
+            const int mid = (int)(int8_t)(c1 & 0xFF);
+            const int hi = (c1 - mid) >> 8;
+            w0 |= (uint32_t)(uint8_t)hi << (8 * bb);
+            w1 |= (uint32_t)(uint8_t)mid << (8 * bb);
+            w2 |= (uint32_t)(uint8_t)lo << (8 * bb);
+        }
+        limbw[0][v] = w0;
+        limbw[1][v] = w1;
+        limbw[2][v] = w2;
+    }
+}
+
 // ---------------------------------------------------------------- stage_kernel
 // One workgroup per token slot tau < kP.  Thread c owns the 16-channel chunk
 // c of the token's row: it loads x and s for its chunk once, the block finds
@@ -264,24 +298,7 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
         const int u = c / 8, grp = (c % 8) / 2, t = c % 2;
         const int wave = u / kUnits, i = u % kUnits;
         uint32_t limbw[3][4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            uint32_t w0 = 0, w1 = 0, w2 = 0;
-#pragma unroll
-            for (int bb = 0; bb < 4; ++bb) {
-                const int cval = (int)rintf(ldexpf(xs[it][frag_offset(v, bb)], -e));
-                const int lo = (int)(int8_t)(cval & 0xFF);
-                const int c1 = (cval - lo) >> 8;
-                const int mid = (int)(int8_t)(c1 & 0xFF);
-                const int hi = (c1 - mid) >> 8;
-                w0 |= (uint32_t)(uint8_t)hi << (8 * bb);
-                w1 |= (uint32_t)(uint8_t)mid << (8 * bb);
-                w2 |= (uint32_t)(uint8_t)lo << (8 * bb);
-            }
-            limbw[0][v] = w0;
-            limbw[1][v] = w1;
-            limbw[2][v] = w2;
-        }
+        split_limbs(xs[it], e, limbw);
         for (int n16 = tau; n16 < 16; n16 += kP) {
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
@@ -608,6 +625,388 @@ verify_kernel(Args a)
         __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ================================================================ batch path
+//
+// Blocks of more than 16 rows (up to 4096: many requests sharing one head).
+// The contraction is then a GEMM of (token, limb) rows against the head,
+// 3M x H times H x V, on the same int8 MFMA and with the same numerics as the
+// single-block kernels (identical codes, exact int32 / int64 sums, one
+// rounding), so a row's results do not depend on the path or the batch it ran
+// in.  The step count grows with M: at M = 256 the 16x16x64 int8 MFMAs, not
+// the weight stream, bound the call.
+//
+//  stage_rows_kernel  codes and step exponents of all rows, written as MFMA
+//      A-operand fragments: for each 16-token block, K step of 128 channels,
+//      half (64 channels) and limb, 64 lanes x 16 bytes contiguous.
+//
+//  verify_rows_kernel  work item = 128 tokens x 128 vocabulary rows over the
+//      whole hidden dimension; workgroups (one per CU) take items
+//      round-robin.  Each of the 8 waves owns one 16-token block (three limb
+//      row blocks) and all 128 rows (8 column blocks): 24 int32 accumulator
+//      tiles.  The weight tile of a K step (128 rows x 64 bytes = 8 KB) is
+//      loaded once per workgroup, one 16-byte chunk per thread, and written
+//      to LDS where every wave reads it; the activation fragments, private to
+//      a wave, go from memory (L2: they are shared by all workgroups) straight
+//      to registers.  Steps of consecutive items form one stream, prefetched
+//      two steps ahead.  At the end of an item each wave turns its
+//      accumulators into logits, reduces them per token and merges the winner
+//      into a per-token 64-bit key with an atomic maximum (value order in the
+//      high word, inverted index in the low word, so the larger value and
+//      then the lower index wins).  The last workgroup decodes the keys,
+//      counts accepted drafts and clears the keys for the next call.
+
+constexpr int kRWaves = 8;                              // waves per workgroup
+constexpr int kRThreads = 64 * kRWaves;                 // 512
+constexpr int kRTokTile = 16 * kRWaves;                 // tokens per work item
+constexpr int kRVocTile = 128;                          // vocabulary rows per work item
+constexpr int kRVBlocks = kRVocTile / 16;               // MFMA column blocks per wave
+constexpr int kRStepH = 128;                            // hidden channels per K step
+constexpr int kRStepBytes = kRVocTile * kRStepH / 2;    // weight tile of one K step
+constexpr int kRStageThreads = 256;
+constexpr int kRStageSteps = 4;                         // K steps per stage workgroup
+static_assert(kRStepBytes == kRThreads * 16, "one 16-byte weight chunk per thread and step");
+
+struct RArgs {
+    const uint16_t *hidden;   // [M, H] binary16
+    const uint8_t *w;         // [V, H/2]
+    const uint16_t *scales;   // [H]
+    const int32_t *draft;     // [R, T-1] or null
+    float *logits_max;        // [M]
+    int32_t *argmax;          // [M]
+    int32_t *n_acc;           // [R]
+    float *logits_out;        // [M, V] or null
+    unsigned long long *keys; // [M] per-token winner keys, zero between calls
+    uint32_t *ticket;
+    int32_t *exps;            // [n_mt * 128] step exponents
+    const u32x4 *frag;        // activation fragments
+    u32x4 *frag_out;
+    int R, T, M, V, H;
+    int n_steps;              // K steps of 128 channels, rounded up to even
+    int n_tb;                 // 16-token blocks that hold real rows: ceil(M / 16)
+    int n_mt;                 // 128-token tiles: ceil(M / 128)
+    int n_items;              // n_mt * ceil(V / 128)
+    unsigned long long w_bytes;
+};
+
+// Index (in 16-byte words) of a fragment: token block tb, K step s, half h,
+// limb l, lane.
+__device__ __forceinline__ size_t rfrag_index(int tb, int n_steps, int s, int h, int l, int lane)
+{
+    return ((((size_t)tb * n_steps + s) * 2 + h) * 3 + l) * 64 + lane;
+}
+
+// XOR swizzle of the four 16-byte chunks of a weight-tile row in LDS (row
+// stride 64 bytes): the 16 rows an MFMA column block reads with one chunk
+// index fall on 16 distinct 16-byte bank groups (8 within any 128 bytes).
+__device__ __forceinline__ int rswz(int r)
+{
+    return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
+}
+
+// Key of a (value, index) pair whose unsigned order is the argmax order:
+// larger value first, then lower index.  -0.0 is keyed as +0.0.
+__device__ __forceinline__ unsigned long long order_key(float v, int i)
+{
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u)
+        u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)i);
+}
+
+__device__ __forceinline__ float key_value(unsigned long long k)
+{
+    const uint32_t u = (uint32_t)(k >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+__device__ __forceinline__ int key_index(unsigned long long k)
+{
+    return (int)(~(uint32_t)k);
+}
+
+// ---------------------------------------------------------------- stage_rows_kernel
+// Grid (token blocks of the padded tiles, groups of kRStageSteps K steps).
+// Every workgroup finds the step exponents of its 16 tokens (the largest
+// |x*s| over the whole row), then writes the fragments of its K steps.
+// Tokens >= M and channels >= H get zero codes.
+__global__ void __launch_bounds__(kRStageThreads) stage_rows_kernel(RArgs a)
+{
+    __shared__ int s_e[16];
+    const int tb = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int H = a.H;
+    {
+        const int n = tid >> 4, sub = tid & 15;   // 16 threads per token
+        const int tok = tb * 16 + n;
+        float am = 0.0f;
+        if (tok < a.M) {
+            const uint16_t *hrow = a.hidden + (size_t)tok * H;
+            for (int c = sub; c * 16 < H; c += 16) {
+                float xs[16];
+                load_xs16(hrow, a.scales, c * 16, xs);
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    am = fmaxf(am, fabsf(xs[j]));
+            }
+        }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1)
+            am = fmaxf(am, __shfl_xor(am, off));
+        if (sub == 0) {
+            const int e = code_exponent(am);
+            s_e[n] = e;
+            if (blockIdx.y == 0)
+                a.exps[tb * 16 + n] = e;
+        }
+    }
+    __syncthreads();
+    const int L = tid & 63, n16 = L & 15, grp = L >> 4;
+    const int tok = tb * 16 + n16;
+    const bool live = tok < a.M;
+    const uint16_t *hrow = a.hidden + (size_t)(live ? tok : 0) * H;
+    const int e = s_e[n16];
+    const int s0 = blockIdx.y * kRStageSteps;
+    for (int p = tid >> 6; p < 2 * kRStageSteps; p += kRStageThreads / 64) {
+        const int s = s0 + (p >> 1), h = p & 1;
+        if (s >= a.n_steps)
+            break;
+        // lane group grp, half h: channels 32*grp + 16*h .. +15 of the step
+        const int ch0 = s * kRStepH + 32 * grp + 16 * h;
+        float xs[16];
+        if (live && ch0 < H) {
+            load_xs16(hrow, a.scales, ch0, xs);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                xs[j] = 0.0f;
+        }
+        uint32_t limbw[3][4];
+        split_limbs(xs, e, limbw);
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+            a.frag_out[rfrag_index(tb, a.n_steps, s, h, l, L)] =
+                u32x4{limbw[l][0], limbw[l][1], limbw[l][2], limbw[l][3]};
+    }
+}
+
+// ---------------------------------------------------------------- verify_rows_kernel
+template <bool kLogits>
+__global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
+{
+    struct Lds {
+        uint8_t wt[2][kRStepBytes];     // weight tiles of the current and the next K step
+        int exp[kBatchMaxRows];         // step exponents of the rows
+        int arg[kBatchMaxRows];         // last workgroup: argmax ids
+        int draft[kBatchMaxRows];       // last workgroup: draft ids
+        int last;
+    };
+    __shared__ __attribute__((aligned(16))) Lds lds;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n16 = lane & 15;   // MFMA row of A / column of B and D
+    const int grp = lane >> 4;   // 16-lane group: K sub-block, D rows 4*grp..4*grp+3
+    const int G = gridDim.x, b = blockIdx.x;
+    const int n_steps = a.n_steps, n_mt = a.n_mt;
+    const int n_my = b < a.n_items ? (a.n_items - 1 - b) / G + 1 : 0;
+
+    for (int m = tid; m < n_mt * kRTokTile; m += kRThreads)
+        lds.exp[m] = a.exps[m];
+    __syncthreads();
+
+    // This thread's weight chunk of every K step: row br of the item's tile,
+    // chunk bc of the step's 64 bytes, stored at LDS slot tid.  Addresses
+    // past the head are clamped (such rows are masked, and channels past H
+    // meet zero codes).
+    const int br = tid >> 2;
+    const int bc = (tid & 3) ^ rswz(br);
+    const unsigned long long w_last = a.w_bytes - 16;
+    const unsigned long long row_bytes = (unsigned long long)(a.H / 2);
+    auto load_w = [&](int k, int s) -> u32x4 {
+        const int nt = (b + k * G) / n_mt;
+        unsigned long long off = (unsigned long long)(nt * kRVocTile + br) * row_bytes +
+                                 (unsigned long long)(s * 64 + bc * 16);
+        off = off < w_last ? off : w_last;
+        return *reinterpret_cast<const u32x4 *>(a.w + off);
+    };
+    auto load_a = [&](int k, int s, i32x4 (&A)[2][3]) {
+        const int tb = ((b + k * G) % n_mt) * kRWaves + wave;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+                A[h][l] = __builtin_bit_cast(i32x4, a.frag[rfrag_index(tb, n_steps, s, h, l, lane)]);
+    };
+    // LDS byte offset of this lane's B fragment in column block vb: row
+    // 16*vb + n16 (the swizzle depends on n16 only), chunk grp
+    const int boff = n16 * 64 + ((grp ^ rswz(n16)) * 16);
+
+    i32x4 acc[3][kRVBlocks];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int l = 0; l < 3; ++l)
+#pragma unroll
+            for (int vb = 0; vb < kRVBlocks; ++vb)
+                acc[l][vb] = i32x4{0, 0, 0, 0};
+    };
+    auto mma_step = [&](const uint8_t *wt, const i32x4 (&A)[2][3]) {
+#pragma unroll
+        for (int vb = 0; vb < kRVBlocks; ++vb) {
+            const u32x4 q = *reinterpret_cast<const u32x4 *>(wt + vb * 1024 + boff);
+            // nibble -> high half of a byte: the int8 value is 16*q
+            const i32x4 b0 = {(int32_t)((q[0] << 4) & 0xF0F0F0F0u), (int32_t)(q[0] & 0xF0F0F0F0u),
+                              (int32_t)((q[1] << 4) & 0xF0F0F0F0u), (int32_t)(q[1] & 0xF0F0F0F0u)};
+            const i32x4 b1 = {(int32_t)((q[2] << 4) & 0xF0F0F0F0u), (int32_t)(q[2] & 0xF0F0F0F0u),
+                              (int32_t)((q[3] << 4) & 0xF0F0F0F0u), (int32_t)(q[3] & 0xF0F0F0F0u)};
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+                acc[l][vb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0][l], b0, acc[l][vb], 0, 0, 0);
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+                acc[l][vb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1][l], b1, acc[l][vb], 0, 0, 0);
+        }
+    };
+    // End of an item: logits of this wave's 16 tokens x 128 rows, the best
+    // per token into its key.
+    auto finish_item = [&](int it) {
+        const int tok0 = ((it % n_mt) * kRWaves + wave) * 16 + 4 * grp;
+        const int vcol = (it / n_mt) * kRVocTile + n16;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = tok0 + r;
+            const int e = lds.exp[tok] - 4;   // weights carry a factor 16
+            float bv = -__builtin_huge_valf();
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int vb = 0; vb < kRVBlocks; ++vb) {
+                const long long code = ((long long)acc[0][vb][r] << 16) +
+                                       ((long long)acc[1][vb][r] << 8) + (long long)acc[2][vb][r];
+                const float val = (float)ldexp((double)code, e);   // the one rounding
+                const int v = vcol + vb * 16;
+                if (v < a.V) {
+                    if (better(val, v, bv, bi)) {
+                        bv = val;
+                        bi = v;
+                    }
+                    if (kLogits && tok < a.M)
+                        a.logits_out[(size_t)tok * a.V + v] = val;
+                }
+            }
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if (n16 == 0 && tok < a.M)
+                __hip_atomic_fetch_max(&a.keys[tok], order_key(bv, bi), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+    };
+
+    // ---------------- the (item, K step) stream, two steps per iteration
+    // Registers: activation fragments of the even and the odd step in
+    // flight (aE, aO), the weight chunk staged for the step after next (wE,
+    // wO).  Steps past the end of the stream re-load the last one (valid
+    // addresses, results unused), which keeps the sequence of memory
+    // operations the same in every iteration.
+    zero_acc();
+    if (n_my > 0) {
+        i32x4 aE[2][3], aO[2][3];
+        load_a(0, 0, aE);
+        u32x4 wE = load_w(0, 0);
+        load_a(0, 1, aO);
+        u32x4 wO = load_w(0, 1);
+        *reinterpret_cast<u32x4 *>(&lds.wt[0][tid * 16]) = wE;
+        int kn = n_steps == 2 ? 1 : 0;     // item and step of the next even step
+        int sn = n_steps == 2 ? 0 : 2;
+        for (int k = 0; k < n_my; ++k) {
+            const bool active = ((b + k * G) % n_mt) * kRWaves + wave < a.n_tb;
+            for (int s = 0; s < n_steps; s += 2) {
+                const int kp = kn < n_my ? kn : n_my - 1;
+                const int sp = kn < n_my ? sn : n_steps - 2;
+                // even step: weights in LDS tile 0, activations in aE
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                barrier_no_fence();
+                wE = load_w(kp, sp);
+                if (active)
+                    mma_step(lds.wt[0], aE);
+                load_a(kp, sp, aE);
+                *reinterpret_cast<u32x4 *>(&lds.wt[1][tid * 16]) = wO;
+                // odd step: weights in LDS tile 1, activations in aO
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                barrier_no_fence();
+                wO = load_w(kp, sp + 1);
+                if (active)
+                    mma_step(lds.wt[1], aO);
+                load_a(kp, sp + 1, aO);
+                *reinterpret_cast<u32x4 *>(&lds.wt[0][tid * 16]) = wE;
+                sn += 2;
+                if (sn == n_steps) {
+                    sn = 0;
+                    ++kn;
+                }
+            }
+            finish_item(b + k * G);
+            zero_acc();
+        }
+    }
+
+    // ---------------- completion: the last workgroup decodes the keys
+    // Each wave's atomics are acknowledged before the ticket is taken (see
+    // verify_kernel for why no fence is used).
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        lds.last = (prev == (uint32_t)(G - 1));
+    }
+    __syncthreads();
+    if (!lds.last)
+        return;
+
+    const int M = a.M;
+    const int n_draft = a.R * (a.T - 1);
+    constexpr int kPer = kBatchMaxRows / kRThreads;
+    unsigned long long key[kPer];
+    int dft[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {   // every load in flight before any is used
+        const int m = tid + j * kRThreads;
+        key[j] = m < M ? __hip_atomic_load(&a.keys[m], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0ull;
+        dft[j] = m < n_draft ? a.draft[m] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int m = tid + j * kRThreads;
+        if (m < M) {
+            const int idx = key_index(key[j]);
+            a.logits_max[m] = key_value(key[j]);
+            a.argmax[m] = idx;
+            lds.arg[m] = idx;
+            __hip_atomic_store(&a.keys[m], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (m < n_draft)
+            lds.draft[m] = dft[j];
+    }
+    __syncthreads();
+    for (int i = tid; i < a.R; i += kRThreads) {
+        const int T = a.T;
+        int n = 0;
+        while (n < T - 1 && lds.arg[i * T + n] == lds.draft[i * (T - 1) + n])
+            ++n;
+        a.n_acc[i] = n;
+    }
+    if (tid == 0)
+        __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // ---------------------------------------------------------------- small kernels
 
 __global__ void fill_zero_u32(uint32_t *p, int n)
@@ -716,13 +1115,24 @@ Pair pick_rows(int M, int units, int *kp)
     return pick<16, kLogits>(units);
 }
 
+// K steps of the batch path (128 channels each, rounded up to even).
+int rows_steps(int H)
+{
+    const int n = (H + kRStepH - 1) / kRStepH;
+    return (n + 1) & ~1;
+}
+
 size_t workspace_need(int R, int T, int V, int H)
 {
     if (R < 1 || T < 1 || T > INT4VH_MAX_T || V < 1 || H < 32 || (H % 32) != 0)
         return 0;
-    if ((long long)R * T > kMaxRows)
+    const long long M = (long long)R * T;
+    if (M > kBatchMaxRows)
         return 0;
-    return kWsBytes;
+    if (M <= kMaxRows)
+        return kWsBytes;
+    const size_t n_mt = (size_t)((M + kRTokTile - 1) / kRTokTile);
+    return kWsFrag + n_mt * kRWaves * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
 }
 
 int validate(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
@@ -731,7 +1141,7 @@ int validate(const void *hidden, const uint8_t *w, const void *scales, const int
 {
     if (R < 1 || T < 1 || T > INT4VH_MAX_T || V < 1 || H < 32 || (H % 32) != 0)
         return INT4VH_EINVAL;
-    if ((long long)R * T > kMaxRows)
+    if ((long long)R * T > kBatchMaxRows)
         return INT4VH_EINVAL;
     if (!hidden || !w || !scales || !lmax || !amax_ids || !nacc || !ws)
         return INT4VH_EINVAL;
@@ -750,6 +1160,55 @@ int validate(const void *hidden, const uint8_t *w, const void *scales, const int
     return INT4VH_OK;
 }
 
+int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
+                int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
+                float *lout, char *wsb, int dev, hipStream_t s)
+{
+    RArgs a;
+    a.hidden = static_cast<const uint16_t *>(hidden);
+    a.w = w;
+    a.scales = static_cast<const uint16_t *>(scales);
+    a.draft = draft;
+    a.logits_max = lmax;
+    a.argmax = amax_ids;
+    a.n_acc = nacc;
+    a.logits_out = lout;
+    a.keys = reinterpret_cast<unsigned long long *>(wsb + kWsKeys);
+    a.ticket = reinterpret_cast<uint32_t *>(wsb + kWsTicket);
+    a.exps = reinterpret_cast<int32_t *>(wsb + kWsExp);
+    a.frag = reinterpret_cast<const u32x4 *>(wsb + kWsFrag);
+    a.frag_out = reinterpret_cast<u32x4 *>(wsb + kWsFrag);
+    a.R = R;
+    a.T = T;
+    a.M = R * T;
+    a.V = V;
+    a.H = H;
+    a.n_steps = rows_steps(H);
+    a.n_tb = (a.M + 15) / 16;
+    a.n_mt = (a.M + kRTokTile - 1) / kRTokTile;
+    const long long n_vt = (V + kRVocTile - 1) / kRVocTile;
+    if ((long long)a.n_mt * n_vt > 0x7FFFFFFFll / 2)
+        return INT4VH_EUNSUPPORTED;
+    a.n_items = (int)(a.n_mt * n_vt);
+    a.w_bytes = (unsigned long long)V * (unsigned long long)(H / 2);
+    int grid = cu_count(dev);
+    if (grid > a.n_items)
+        grid = a.n_items;
+    const dim3 stage_grid(a.n_mt * kRWaves, (a.n_steps + kRStageSteps - 1) / kRStageSteps);
+    hipLaunchKernelGGL(stage_rows_kernel, stage_grid, dim3(kRStageThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "stage_rows kernel launch");
+    if (lout)
+        hipLaunchKernelGGL(verify_rows_kernel<true>, dim3(grid), dim3(kRThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL(verify_rows_kernel<false>, dim3(grid), dim3(kRThreads), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "verify_rows kernel launch");
+    return INT4VH_OK;
+}
+
 int launch_verify(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
                   int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
                   float *lout, void *ws, size_t ws_bytes, void *stream)
@@ -764,6 +1223,10 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
         return hip_fail(e, "hipGetDevice");
 
     char *wsb = static_cast<char *>(ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (R * T > kMaxRows)
+        return launch_rows(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, wsb,
+                           dev, s);
     Args a;
     a.hidden = static_cast<const uint16_t *>(hidden);
     a.w = w;
@@ -794,7 +1257,6 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
         grid = a.n_tiles;
     int kp = 16;
     const Pair fn = lout ? pick_rows<true>(a.M, units, &kp) : pick_rows<false>(a.M, units, &kp);
-    const hipStream_t s = static_cast<hipStream_t>(stream);
     hipLaunchKernelGGL(fn.stage, dim3(kp), dim3(kStageThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess)
@@ -821,11 +1283,11 @@ int verify_lm_head_int4_workspace_init(void *ws, size_t ws_bytes, void *stream)
         return INT4VH_EINVAL;
     if (!aligned(ws, 256))
         return INT4VH_EALIGN;
-    if (ws_bytes < kWsPart)
+    if (ws_bytes < kWsCtlBytes)
         return INT4VH_EWORKSPACE;
-    const int n = (int)(kWsPart / sizeof(uint32_t));
-    hipLaunchKernelGGL(fill_zero_u32, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
-                       static_cast<uint32_t *>(ws), n);
+    const int n = (int)(kWsCtlBytes / sizeof(uint32_t));
+    hipLaunchKernelGGL(fill_zero_u32, dim3((n + 255) / 256), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint32_t *>(ws), n);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "workspace init launch");

@@ -98,10 +98,39 @@ def test_draft_may_be_null_only_for_T1(lib):
 
 
 def test_batch_rejects_invalid(lib):
+    """Every call here fails host validation, so nothing is launched on the
+    fake pointers."""
     P = ctypes.c_void_p
     f = lib.verify_lm_head_int4_batch
-    assert f(P(A), P(A), P(A), P(A), 0, 4, 10, 64, P(A), P(A), P(A), None, P(A), WS, None) == EINVAL
-    assert f(P(A), P(A), P(A), P(A), 5, 4, 10, 64, P(A), P(A), P(A), None, P(A), WS, None) == EINVAL
+
+    def bcall(R, T, V=10, H=64, ws_bytes=WS, d=A):
+        return f(P(A), P(A), P(A), P(d), R, T, V, H, P(A), P(A), P(A), None, P(A), ws_bytes, None)
+
+    assert bcall(0, 4) == EINVAL
+    assert bcall(4097, 1) == EINVAL           # more than 4096 rows
+    assert bcall(257, 16) == EINVAL
+    assert bcall(-3, 4) == EINVAL
+    assert bcall(64, 17) == EINVAL
+    assert bcall(64, 4, d=0) == EINVAL        # drafts required for T > 1
+    need = lib.verify_lm_head_int4_workspace_bytes(64, 4, 151936, 5120)
+    assert bcall(64, 4, 151936, 5120, ws_bytes=need - 256) == EWORKSPACE
+    assert bcall(64, 4, 151936, 5120, ws_bytes=need, d=A + 2) == EALIGN
+
+
+def test_batch_workspace_bytes(lib):
+    wb = lib.verify_lm_head_int4_workspace_bytes
+    assert wb(4097, 1, 10, 64) == 0 and wb(257, 16, 10, 64) == 0
+    small = wb(1, 16, 151936, 5120)
+    # up to 16 rows: the single-block layout; beyond: activation fragments
+    # of 128-row tiles, 3 bytes per row and (padded) channel
+    assert wb(4, 4, 151936, 5120) == small
+    big = wb(64, 4, 151936, 5120)
+    assert big > small and big % 256 == 0
+    assert wb(256, 16, 10, 64) > 0
+    per_tile = (wb(256, 1, 10, 5120) - wb(128, 1, 10, 5120))
+    assert per_tile == 128 * 5120 * 3
+    assert wb(129, 1, 10, 5120) == wb(256, 1, 10, 5120)
+    assert wb(17, 1, 10, 5120) == wb(128, 1, 10, 5120)
 
 
 def test_workspace_init_and_check_weights_validation(lib):

@@ -30,3 +30,22 @@ def test_stored_argmax_matches_oracle(oracle_mod, name, trials):
         rec = data["trials"][str(t)]
         assert idx.tolist() == rec["argmax"]
         assert np.allclose(gap, rec["gap"]) and np.allclose(amax, rec["amax"])
+
+
+def test_stored_batch_argmax_rows_match_oracle(oracle_mod):
+    """The 64 x 4 batch file, checked on a few rows of two trials (the whole
+    file takes the oracle minutes)."""
+    cfg = synth.CONFIGS["batch"]
+    data = _load("batch")
+    assert (data["V"], data["H"], data["R"], data["T"]) == (cfg.V, cfg.H, cfg.R, cfg.T)
+    head = synth.make_head(cfg)
+    rows = [0, 101, 255]
+    for t in (0, 4):
+        x = synth.make_hidden(cfg, t).reshape(cfg.M, cfg.H)
+        lg = oracle_mod.logits(np.ascontiguousarray(x[rows]), head["packed"], head["scales"],
+                               len(rows), cfg.V, cfg.H)
+        idx, _, gap, amax = oracle_mod.argmax_rows(lg)
+        rec = data["trials"][str(t)]
+        assert idx.tolist() == [rec["argmax"][r] for r in rows]
+        assert np.allclose(gap, [rec["gap"][r] for r in rows])
+        assert np.allclose(amax, [rec["amax"][r] for r in rows])
