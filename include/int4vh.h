@@ -37,13 +37,19 @@
  *   logits_max float32 [M]; argmax_ids int32 [M]; n_accepted int32 [R]
  *   logits_out optional float32 [M, V] (every logit; NULL to skip)
  *
- * Numerics.  Products use the exact value of hidden*scale rounded to a
- * 16-bit fixed-point code per row (a power-of-two step of at most 2^-14 of
- * the row's largest |hidden*scale|), multiplied by the exact int4 weights in
- * int8 matrix cores with exact int32 accumulation; each logit is rounded to
+ * Numerics.  For each row, hidden*scale (exact in binary32) is rounded to a
+ * 24-bit fixed-point code with a power-of-two step chosen from the row's
+ * largest |hidden*scale| (the step is at most 2^-22 of it; round to nearest
+ * even).  Each code is split into three signed bytes, the int4 weights enter
+ * the int8 matrix cores exactly, the int32 partial sums are exact and are
+ * combined exactly in 64-bit integers, and each logit is rounded to
  * binary32 once.  The absolute error of a logit is below
- * 2^-15 * max_h|hidden*scale| * sum_h|q[v,h]|, and every result is
- * independent of the launch shape and bit-for-bit reproducible.
+ *   2^-23 * max_h|hidden*scale| * sum_h|q[v,h]|   (+ the final rounding),
+ * far inside the 2e-3 * max_v|logit| parity tolerance.  Every result is
+ * bit-for-bit reproducible and independent of the launch shape: a row gives
+ * the same logits, argmax and maximum whether it runs alone, in a block of
+ * up to 16 rows (the weight-stream kernel) or in a batch of up to 4096 rows
+ * (the MFMA-bound batch kernel).
  *
  * Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL is
  * the null stream).  Results are valid once the caller synchronises that
@@ -59,9 +65,9 @@
  * Errors.  Every entry point returns a status code; nothing is thrown across
  * the ABI.  Arguments are validated on the host before anything is launched
  * (no GPU call happens when validation fails):
- *   INT4VH_EINVAL       T outside [1, 16]; R < 1; R*T > 16 for the
- *                       single-block kernels of this version; V < 1; H < 32
- *                       or H % 32 != 0; a required pointer is NULL
+ *   INT4VH_EINVAL       T outside [1, 16]; R < 1; R*T > 4096
+ *                       (INT4VH_MAX_ROWS); V < 1; H < 32 or H % 32 != 0; a
+ *                       required pointer is NULL
  *   INT4VH_EALIGN       a tensor pointer is not 16-byte aligned (workspace:
  *                       256-byte aligned)
  *   INT4VH_EWORKSPACE   workspace smaller than required
@@ -93,6 +99,8 @@ enum {
 #define INT4VH_MAX_H 8192
 /* Largest T (verify positions per request). */
 #define INT4VH_MAX_T 16
+/* Largest number of rows R*T of one call. */
+#define INT4VH_MAX_ROWS 4096
 
 /* Bytes of workspace a verify call with these sizes needs (0 if the sizes are
  * invalid).  Pure host function. */
@@ -113,12 +121,31 @@ int verify_lm_head_int4(const void *hidden, const uint8_t *packed_w, const void 
 
 /* R independent requests of T positions each, sharing one head.  Rows of
  * request i are hidden[i*T .. i*T+T-1]; its drafts are draft_ids[i*(T-1) ..].
- * Per-request acceptance goes to n_accepted[i]. */
+ * Per-request acceptance goes to n_accepted[i].  Up to 16 rows the call runs
+ * the weight-stream kernels; beyond, up to INT4VH_MAX_ROWS rows, it runs a
+ * GEMM on the int8 matrix cores whose workspace grows with R*T
+ * (verify_lm_head_int4_workspace_bytes).  The batch mode of the HyperQwen
+ * README, "The numbers behind that", serves 64 requests at once: 64 x 4 =
+ * 256 rows.  Results are identical either way. */
 int verify_lm_head_int4_batch(const void *hidden, const uint8_t *packed_w, const void *scales,
                               const int32_t *draft_ids, int R, int T, int V, int H,
                               float *logits_max, int32_t *argmax_ids, int32_t *n_accepted,
                               float *logits_out, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/* The batch call, instrumented: event_before and event_after (hipEvent_t
+ * handles owned by the caller, created on the stream's device; NULL skips a
+ * record) are recorded on `stream` immediately before and after the main
+ * verify kernel, after the staging kernel, so that hipEventElapsedTime gives
+ * the main kernel's duration alone.  Same arguments, results and errors as
+ * verify_lm_head_int4_batch; a failed record returns INT4VH_EHIP.  For
+ * measuring the weight stream (or the matrix cores) against its roofline. */
+int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
+                                    const void *scales, const int32_t *draft_ids, int R, int T,
+                                    int V, int H, float *logits_max, int32_t *argmax_ids,
+                                    int32_t *n_accepted, float *logits_out, void *workspace,
+                                    size_t workspace_bytes, void *stream, void *event_before,
+                                    void *event_after);
 
 /* Count illegal nibbles (0x8) of a packed head into *n_bad_out (device int32,
  * overwritten).  Asynchronous on `stream`. */

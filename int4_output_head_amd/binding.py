@@ -42,6 +42,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.verify_lm_head_int4_batch.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P, P,
                                                 sz, P]
         L.verify_lm_head_int4_batch.restype = i32
+        L.verify_lm_head_int4_batch_timed.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P,
+                                                      P, sz, P, P, P]
+        L.verify_lm_head_int4_batch_timed.restype = i32
         L.verify_lm_head_int4_check_weights.argtypes = [P, i32, i32, P, P]
         L.verify_lm_head_int4_check_weights.restype = i32
         L.verify_lm_head_int4_status_string.argtypes = [i32]
@@ -109,12 +112,22 @@ def _check(t, name, dtype, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
+def _event_handle(ev, stream):
+    """Raw hipEvent_t of a torch.cuda.Event (created by a first record)."""
+    if ev.cuda_event == 0:
+        ev.record(stream)
+    return ctypes.c_void_p(ev.cuda_event)
+
+
 def verify_batch(hidden, packed_w, scales, draft_ids=None, *, R: int | None = None,
-                 logits: bool = False, workspace: Workspace | None = None):
+                 logits: bool = False, workspace: Workspace | None = None, events=None):
     """R requests x T positions.  hidden: float16 [R, T, H] (or [R*T, H] with
     R given); packed_w: uint8 [V, H/2]; scales: float16 [H]; draft_ids: int32
     [R, T-1] (None when T == 1).  Returns (logits_max [R*T], argmax_ids [R*T],
-    n_accepted [R]) and, with logits=True, logits [R*T, V] as a 4th item."""
+    n_accepted [R]) and, with logits=True, logits [R*T, V] as a 4th item.
+    events=(before, after), two torch.cuda.Event(enable_timing=True), are
+    recorded on the current stream right around the main verify kernel (the
+    instrumented entry point verify_lm_head_int4_batch_timed)."""
     if hidden.dim() == 3:
         R, T, H = hidden.shape
         hidden = hidden.reshape(R * T, H)
@@ -148,9 +161,14 @@ def verify_batch(hidden, packed_w, scales, draft_ids=None, *, R: int | None = No
     if need == 0:
         _raise(EINVAL, "verify")
     ws = workspace if workspace is not None else _default_workspace(dev, need)
-    st = L.verify_lm_head_int4_batch(_ptr(hidden), _ptr(packed_w), _ptr(scales), _ptr(draft_ids),
-                                     R, T, V, H, _ptr(lmax), _ptr(amax), _ptr(nacc), _ptr(lout),
-                                     _ptr(ws.tensor), ws.nbytes, _stream_ptr(dev))
+    args = (_ptr(hidden), _ptr(packed_w), _ptr(scales), _ptr(draft_ids), R, T, V, H, _ptr(lmax),
+            _ptr(amax), _ptr(nacc), _ptr(lout), _ptr(ws.tensor), ws.nbytes, _stream_ptr(dev))
+    if events is None:
+        st = L.verify_lm_head_int4_batch(*args)
+    else:
+        stream = torch.cuda.current_stream(dev)
+        st = L.verify_lm_head_int4_batch_timed(*args, _event_handle(events[0], stream),
+                                               _event_handle(events[1], stream))
     if st != OK:
         _raise(st, "verify_lm_head_int4_batch")
     return (lmax, amax, nacc, lout) if logits else (lmax, amax, nacc)

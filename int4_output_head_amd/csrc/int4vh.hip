@@ -641,30 +641,44 @@ verify_kernel(Args a)
 //
 //  verify_rows_kernel  work item = 128 tokens x 128 vocabulary rows over the
 //      whole hidden dimension; workgroups (one per CU) take items
-//      round-robin.  Each of the 8 waves owns one 16-token block (three limb
-//      row blocks) and all 128 rows (8 column blocks): 24 int32 accumulator
-//      tiles.  The weight tile of a K step (128 rows x 64 bytes = 8 KB) is
-//      loaded once per workgroup, one 16-byte chunk per thread, and written
-//      to LDS where every wave reads it; the activation fragments, private to
-//      a wave, go from memory (L2: they are shared by all workgroups) straight
-//      to registers.  Steps of consecutive items form one stream, prefetched
-//      two steps ahead.  At the end of an item each wave turns its
-//      accumulators into logits, reduces them per token and merges the winner
-//      into a per-token 64-bit key with an atomic maximum (value order in the
-//      high word, inverted index in the low word, so the larger value and
-//      then the lower index wins).  The last workgroup decodes the keys,
-//      counts accepted drafts and clears the keys for the next call.
+//      round-robin.  Each of the 8 waves (two per SIMD) owns one 16-token
+//      block (three limb row blocks) and all 128 rows (8 column blocks): 24
+//      int32 accumulator tiles.  The packed weights of a K step (128 rows x
+//      64 bytes) are loaded once per workgroup, one 16-byte chunk per thread,
+//      turned into int8 B fragments by the thread that loaded them and
+//      written to LDS (16 KB, double-buffered), where every wave reads them:
+//      the nibble conversion happens once per workgroup, not once per wave.
+//      The activation fragments, private to a wave, go from memory (L2:
+//      every workgroup reads them) straight to registers.  Steps of
+//      consecutive items form one stream, prefetched two steps ahead.  At the
+//      end of an item each wave turns its accumulators into logits, reduces
+//      them per token and merges the winner into a per-token 64-bit key with
+//      an atomic maximum (value order in the high word, inverted index in the
+//      low word, so the larger value and then the lower index wins).  The
+//      last workgroup decodes the keys, counts accepted drafts and clears the
+//      keys for the next call.
+//
+// Alternatives that measured slower on MI355X: four waves of 32 tokens (one
+// per SIMD: LDS and memory latency exposed with no second wave to cover
+// it), per-wave nibble conversion from a packed LDS tile (the VALU work
+// equals the MFMA issue time), a four-deep register ring (no gain: the stalls
+// are not latency), and activation re-loads interleaved between MFMAs (a
+// load into a register that in-flight MFMAs still read stalls the wave).
 
 constexpr int kRWaves = 8;                              // waves per workgroup
-constexpr int kRThreads = 64 * kRWaves;                 // 512
-constexpr int kRTokTile = 16 * kRWaves;                 // tokens per work item
+constexpr int kRThreads = 64 * kRWaves;
+constexpr int kRTbPerWave = 8 / kRWaves;                // 16-token blocks per wave
+constexpr int kRTbPerTile = kRTbPerWave * kRWaves;      // 16-token blocks per work item
+constexpr int kRTokTile = 16 * kRTbPerTile;             // tokens per work item
 constexpr int kRVocTile = 128;                          // vocabulary rows per work item
 constexpr int kRVBlocks = kRVocTile / 16;               // MFMA column blocks per wave
 constexpr int kRStepH = 128;                            // hidden channels per K step
-constexpr int kRStepBytes = kRVocTile * kRStepH / 2;    // weight tile of one K step
+constexpr int kRStepBytes = kRVocTile * kRStepH / 2;    // packed weight bytes of one K step
+constexpr int kRTileBytes = kRVocTile * kRStepH;        // the same weights as int8 MFMA fragments
 constexpr int kRStageThreads = 256;
 constexpr int kRStageSteps = 4;                         // K steps per stage workgroup
-static_assert(kRStepBytes == kRThreads * 16, "one 16-byte weight chunk per thread and step");
+constexpr int kRChunks = kRStepBytes / (kRThreads * 16);   // 16-byte weight chunks per thread and step
+static_assert(kRChunks * kRWaves == kRVBlocks, "each wave stages whole column blocks");
 
 struct RArgs {
     const uint16_t *hidden;   // [M, H] binary16
@@ -693,14 +707,6 @@ struct RArgs {
 __device__ __forceinline__ size_t rfrag_index(int tb, int n_steps, int s, int h, int l, int lane)
 {
     return ((((size_t)tb * n_steps + s) * 2 + h) * 3 + l) * 64 + lane;
-}
-
-// XOR swizzle of the four 16-byte chunks of a weight-tile row in LDS (row
-// stride 64 bytes): the 16 rows an MFMA column block reads with one chunk
-// index fall on 16 distinct 16-byte bank groups (8 within any 128 bytes).
-__device__ __forceinline__ int rswz(int r)
-{
-    return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
 }
 
 // Key of a (value, index) pair whose unsigned order is the argmax order:
@@ -795,7 +801,7 @@ template <bool kLogits>
 __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
 {
     struct Lds {
-        uint8_t wt[2][kRStepBytes];     // weight tiles of the current and the next K step
+        uint8_t wt[2][kRTileBytes];     // int8 weight fragments of the current and the next K step
         int exp[kBatchMaxRows];         // step exponents of the rows
         int arg[kBatchMaxRows];         // last workgroup: argmax ids
         int draft[kBatchMaxRows];       // last workgroup: draft ids
@@ -815,136 +821,173 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
         lds.exp[m] = a.exps[m];
     __syncthreads();
 
-    // This thread's weight chunk of every K step: row br of the item's tile,
-    // chunk bc of the step's 64 bytes, stored at LDS slot tid.  Addresses
-    // past the head are clamped (such rows are masked, and channels past H
-    // meet zero codes).
-    const int br = tid >> 2;
-    const int bc = (tid & 3) ^ rswz(br);
+    // Weight chunks of this thread in every K step: 16 bytes (32 channels)
+    // of rows 16*(wave + kRWaves*j) + n16 of the item's tile, chunk grp of
+    // the step's 64 bytes, j < kRChunks.  The chunk becomes exactly the B fragment
+    // words of this lane for column block wave + kRWaves*j, halves 0 and 1, so
+    // each wave converts and stores whole 1 KB fragments.  Addresses past
+    // the head are clamped (such rows are masked, and channels past H meet
+    // zero codes).
     const unsigned long long w_last = a.w_bytes - 16;
     const unsigned long long row_bytes = (unsigned long long)(a.H / 2);
-    auto load_w = [&](int k, int s) -> u32x4 {
+    auto load_w = [&](int k, int s, u32x4 (&q)[kRChunks]) {
         const int nt = (b + k * G) / n_mt;
-        unsigned long long off = (unsigned long long)(nt * kRVocTile + br) * row_bytes +
-                                 (unsigned long long)(s * 64 + bc * 16);
-        off = off < w_last ? off : w_last;
-        return *reinterpret_cast<const u32x4 *>(a.w + off);
-    };
-    auto load_a = [&](int k, int s, i32x4 (&A)[2][3]) {
-        const int tb = ((b + k * G) % n_mt) * kRWaves + wave;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int l = 0; l < 3; ++l)
-                A[h][l] = __builtin_bit_cast(i32x4, a.frag[rfrag_index(tb, n_steps, s, h, l, lane)]);
-    };
-    // LDS byte offset of this lane's B fragment in column block vb: row
-    // 16*vb + n16 (the swizzle depends on n16 only), chunk grp
-    const int boff = n16 * 64 + ((grp ^ rswz(n16)) * 16);
-
-    i32x4 acc[3][kRVBlocks];
-    auto zero_acc = [&]() {
-#pragma unroll
-        for (int l = 0; l < 3; ++l)
-#pragma unroll
-            for (int vb = 0; vb < kRVBlocks; ++vb)
-                acc[l][vb] = i32x4{0, 0, 0, 0};
-    };
-    auto mma_step = [&](const uint8_t *wt, const i32x4 (&A)[2][3]) {
-#pragma unroll
-        for (int vb = 0; vb < kRVBlocks; ++vb) {
-            const u32x4 q = *reinterpret_cast<const u32x4 *>(wt + vb * 1024 + boff);
-            // nibble -> high half of a byte: the int8 value is 16*q
-            const i32x4 b0 = {(int32_t)((q[0] << 4) & 0xF0F0F0F0u), (int32_t)(q[0] & 0xF0F0F0F0u),
-                              (int32_t)((q[1] << 4) & 0xF0F0F0F0u), (int32_t)(q[1] & 0xF0F0F0F0u)};
-            const i32x4 b1 = {(int32_t)((q[2] << 4) & 0xF0F0F0F0u), (int32_t)(q[2] & 0xF0F0F0F0u),
-                              (int32_t)((q[3] << 4) & 0xF0F0F0F0u), (int32_t)(q[3] & 0xF0F0F0F0u)};
-#pragma unroll
-            for (int l = 0; l < 3; ++l)
-                acc[l][vb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[0][l], b0, acc[l][vb], 0, 0, 0);
-#pragma unroll
-            for (int l = 0; l < 3; ++l)
-                acc[l][vb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[1][l], b1, acc[l][vb], 0, 0, 0);
+        for (int j = 0; j < kRChunks; ++j) {
+            unsigned long long off =
+                (unsigned long long)(nt * kRVocTile + 16 * (wave + kRWaves * j) + n16) * row_bytes +
+                (unsigned long long)(s * 64 + grp * 16);
+            off = off < w_last ? off : w_last;
+            q[j] = *reinterpret_cast<const u32x4 *>(a.w + off);
         }
     };
-    // End of an item: logits of this wave's 16 tokens x 128 rows, the best
-    // per token into its key.
+    // nibble -> high half of a byte: the int8 value is 16*q; fragment word
+    // (half h, column block vb) of lane L sits at byte ((8h + vb) * 64 + L) * 16
+    auto store_w = [&](uint8_t *wt, const u32x4 (&q)[kRChunks]) {
+#pragma unroll
+        for (int j = 0; j < kRChunks; ++j) {
+            const int vb = wave + kRWaves * j;
+            const i32x4 b0 = {(int32_t)((q[j][0] << 4) & 0xF0F0F0F0u), (int32_t)(q[j][0] & 0xF0F0F0F0u),
+                              (int32_t)((q[j][1] << 4) & 0xF0F0F0F0u), (int32_t)(q[j][1] & 0xF0F0F0F0u)};
+            const i32x4 b1 = {(int32_t)((q[j][2] << 4) & 0xF0F0F0F0u), (int32_t)(q[j][2] & 0xF0F0F0F0u),
+                              (int32_t)((q[j][3] << 4) & 0xF0F0F0F0u), (int32_t)(q[j][3] & 0xF0F0F0F0u)};
+            *reinterpret_cast<i32x4 *>(wt + (vb * 64 + lane) * 16) = b0;
+            *reinterpret_cast<i32x4 *>(wt + ((8 + vb) * 64 + lane) * 16) = b1;
+        }
+    };
+    // activation fragments of one half (64 channels) of a K step
+    auto load_a = [&](int k, int s, int h, i32x4 (&A)[kRTbPerWave][2][3]) {
+        const int tb0 = ((b + k * G) % n_mt) * kRTbPerTile + wave * kRTbPerWave;
+#pragma unroll
+        for (int t = 0; t < kRTbPerWave; ++t)
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+                A[t][h][l] = __builtin_bit_cast(
+                    i32x4, a.frag[rfrag_index(tb0 + t, n_steps, s, h, l, lane)]);
+    };
+
+    i32x4 acc[kRTbPerWave][3][kRVBlocks];
+    auto zero_acc = [&]() {
+#pragma unroll
+        for (int t = 0; t < kRTbPerWave; ++t)
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+#pragma unroll
+                for (int vb = 0; vb < kRVBlocks; ++vb)
+                    acc[t][l][vb] = i32x4{0, 0, 0, 0};
+    };
+    // One half (64 channels) of a K step over all column blocks.  The eight
+    // B fragments are read from LDS before the first MFMA needs one (the
+    // schedule is pinned: left alone, the compiler keeps only two reads in
+    // flight and waits on each).
+    auto mma_half = [&](const uint8_t *wt, int h, const i32x4 (&A)[kRTbPerWave][2][3]) {
+        i32x4 bf[kRVBlocks];
+#pragma unroll
+        for (int vb = 0; vb < kRVBlocks; ++vb)
+            bf[vb] = *reinterpret_cast<const i32x4 *>(wt + ((8 * h + vb) * 64 + lane) * 16);
+#pragma unroll
+        for (int vb = 0; vb < kRVBlocks; ++vb)
+#pragma unroll
+            for (int t = 0; t < kRTbPerWave; ++t)
+#pragma unroll
+                for (int l = 0; l < 3; ++l)
+                    acc[t][l][vb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[t][h][l], bf[vb], acc[t][l][vb], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0100, kRVBlocks, 0);                    // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x0008, kRVBlocks * kRTbPerWave * 3, 0);  // MFMAs
+    };
+    // End of an item: logits of this wave's 32 tokens x 128 rows, the best
+    // per token into its key.  The limbs combine exactly in binary64
+    // (|code| < 2^53); the one rounding to binary32 happens before the
+    // power-of-two step is applied, which gives the same value because the
+    // scaled logits stay in the normal range.  Within a lane the column
+    // index grows with vb, so a strict > keeps the lowest index on ties.
     auto finish_item = [&](int it) {
-        const int tok0 = ((it % n_mt) * kRWaves + wave) * 16 + 4 * grp;
         const int vcol = (it / n_mt) * kRVocTile + n16;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int tok = tok0 + r;
-            const int e = lds.exp[tok] - 4;   // weights carry a factor 16
-            float bv = -__builtin_huge_valf();
-            int bi = 0x7FFFFFFF;
+        for (int t = 0; t < kRTbPerWave; ++t) {
+            const int tok0 = ((it % n_mt) * kRTbPerTile + wave * kRTbPerWave + t) * 16 + 4 * grp;
 #pragma unroll
-            for (int vb = 0; vb < kRVBlocks; ++vb) {
-                const long long code = ((long long)acc[0][vb][r] << 16) +
-                                       ((long long)acc[1][vb][r] << 8) + (long long)acc[2][vb][r];
-                const float val = (float)ldexp((double)code, e);   // the one rounding
-                const int v = vcol + vb * 16;
-                if (v < a.V) {
-                    if (better(val, v, bv, bi)) {
-                        bv = val;
-                        bi = v;
-                    }
-                    if (kLogits && tok < a.M)
-                        a.logits_out[(size_t)tok * a.V + v] = val;
-                }
-            }
+            for (int r = 0; r < 4; ++r) {
+                const int tok = tok0 + r;
+                const int e = lds.exp[tok] - 4;   // weights carry a factor 16
+                float bv = -__builtin_huge_valf();
+                int bi = 0x7FFFFFFF;
 #pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (better(ov, oi, bv, bi)) {
-                    bv = ov;
-                    bi = oi;
+                for (int vb = 0; vb < kRVBlocks; ++vb) {
+                    const double code = __builtin_fma((double)acc[t][0][vb][r], 65536.0,
+                                                      __builtin_fma((double)acc[t][1][vb][r], 256.0,
+                                                                    (double)acc[t][2][vb][r]));
+                    const float u = (float)code;          // the one rounding
+                    const int v = vcol + vb * 16;
+                    const bool take = v < a.V && u > bv;
+                    bv = take ? u : bv;
+                    bi = take ? v : bi;
+                    if (kLogits && tok < a.M && v < a.V)
+                        a.logits_out[(size_t)tok * a.V + v] = ldexpf(u, e);
                 }
+#pragma unroll
+                for (int off = 8; off >= 1; off >>= 1) {
+                    const float ov = __shfl_xor(bv, off);
+                    const int oi = __shfl_xor(bi, off);
+                    const bool take = ov > bv || (ov == bv && oi < bi);
+                    bv = take ? ov : bv;
+                    bi = take ? oi : bi;
+                }
+                if (n16 == 0 && tok < a.M)
+                    __hip_atomic_fetch_max(&a.keys[tok], order_key(ldexpf(bv, e), bi),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            if (n16 == 0 && tok < a.M)
-                __hip_atomic_fetch_max(&a.keys[tok], order_key(bv, bi), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
         }
     };
 
     // ---------------- the (item, K step) stream, two steps per iteration
     // Registers: activation fragments of the even and the odd step in
-    // flight (aE, aO), the weight chunk staged for the step after next (wE,
-    // wO).  Steps past the end of the stream re-load the last one (valid
-    // addresses, results unused), which keeps the sequence of memory
-    // operations the same in every iteration.
+    // flight (aE, aO), the packed weight chunks staged for the step after
+    // next (wE, wO).  Steps past the end of the stream re-load the last one
+    // (valid addresses, results unused), which keeps the sequence of memory
+    // operations the same in every iteration.  n_steps is even, so items
+    // start at an even step.
     zero_acc();
     if (n_my > 0) {
-        i32x4 aE[2][3], aO[2][3];
-        load_a(0, 0, aE);
-        u32x4 wE = load_w(0, 0);
-        load_a(0, 1, aO);
-        u32x4 wO = load_w(0, 1);
-        *reinterpret_cast<u32x4 *>(&lds.wt[0][tid * 16]) = wE;
+        i32x4 aE[kRTbPerWave][2][3], aO[kRTbPerWave][2][3];
+        u32x4 wE[kRChunks], wO[kRChunks];
+        load_a(0, 0, 0, aE);
+        load_a(0, 0, 1, aE);
+        load_w(0, 0, wE);
+        load_a(0, 1, 0, aO);
+        load_a(0, 1, 1, aO);
+        load_w(0, 1, wO);
+        store_w(lds.wt[0], wE);
         int kn = n_steps == 2 ? 1 : 0;     // item and step of the next even step
         int sn = n_steps == 2 ? 0 : 2;
         for (int k = 0; k < n_my; ++k) {
-            const bool active = ((b + k * G) % n_mt) * kRWaves + wave < a.n_tb;
+            const bool active =
+                ((b + k * G) % n_mt) * kRTbPerTile + wave * kRTbPerWave < a.n_tb;
             for (int s = 0; s < n_steps; s += 2) {
                 const int kp = kn < n_my ? kn : n_my - 1;
                 const int sp = kn < n_my ? sn : n_steps - 2;
                 // even step: weights in LDS tile 0, activations in aE
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                 barrier_no_fence();
-                wE = load_w(kp, sp);
+                load_w(kp, sp, wE);
                 if (active)
-                    mma_step(lds.wt[0], aE);
-                load_a(kp, sp, aE);
-                *reinterpret_cast<u32x4 *>(&lds.wt[1][tid * 16]) = wO;
+                    mma_half(lds.wt[0], 0, aE);
+                load_a(kp, sp, 0, aE);
+                if (active)
+                    mma_half(lds.wt[0], 1, aE);
+                load_a(kp, sp, 1, aE);
+                store_w(lds.wt[1], wO);
                 // odd step: weights in LDS tile 1, activations in aO
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                 barrier_no_fence();
-                wO = load_w(kp, sp + 1);
+                load_w(kp, sp + 1, wO);
                 if (active)
-                    mma_step(lds.wt[1], aO);
-                load_a(kp, sp + 1, aO);
-                *reinterpret_cast<u32x4 *>(&lds.wt[0][tid * 16]) = wE;
+                    mma_half(lds.wt[1], 0, aO);
+                load_a(kp, sp + 1, 0, aO);
+                if (active)
+                    mma_half(lds.wt[1], 1, aO);
+                load_a(kp, sp + 1, 1, aO);
+                store_w(lds.wt[0], wE);
                 sn += 2;
                 if (sn == n_steps) {
                     sn = 0;
@@ -1132,7 +1175,7 @@ size_t workspace_need(int R, int T, int V, int H)
     if (M <= kMaxRows)
         return kWsBytes;
     const size_t n_mt = (size_t)((M + kRTokTile - 1) / kRTokTile);
-    return kWsFrag + n_mt * kRWaves * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
+    return kWsFrag + n_mt * kRTbPerTile * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
 }
 
 int validate(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
@@ -1160,9 +1203,18 @@ int validate(const void *hidden, const uint8_t *w, const void *scales, const int
     return INT4VH_OK;
 }
 
+// Records ev (a hipEvent_t, may be null) on stream s.
+int record_event(void *ev, hipStream_t s, const char *what)
+{
+    if (!ev)
+        return INT4VH_OK;
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev), s);
+    return e == hipSuccess ? INT4VH_OK : hip_fail(e, what);
+}
+
 int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
                 int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
-                float *lout, char *wsb, int dev, hipStream_t s)
+                float *lout, char *wsb, int dev, hipStream_t s, void *ev0, void *ev1)
 {
     RArgs a;
     a.hidden = static_cast<const uint16_t *>(hidden);
@@ -1194,11 +1246,14 @@ int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const 
     int grid = cu_count(dev);
     if (grid > a.n_items)
         grid = a.n_items;
-    const dim3 stage_grid(a.n_mt * kRWaves, (a.n_steps + kRStageSteps - 1) / kRStageSteps);
+    const dim3 stage_grid(a.n_mt * kRTbPerTile, (a.n_steps + kRStageSteps - 1) / kRStageSteps);
     hipLaunchKernelGGL(stage_rows_kernel, stage_grid, dim3(kRStageThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "stage_rows kernel launch");
+    int st = record_event(ev0, s, "event record before verify_rows kernel");
+    if (st != INT4VH_OK)
+        return st;
     if (lout)
         hipLaunchKernelGGL(verify_rows_kernel<true>, dim3(grid), dim3(kRThreads), 0, s, a);
     else
@@ -1206,12 +1261,13 @@ int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const 
     e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "verify_rows kernel launch");
-    return INT4VH_OK;
+    return record_event(ev1, s, "event record after verify_rows kernel");
 }
 
 int launch_verify(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
                   int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
-                  float *lout, void *ws, size_t ws_bytes, void *stream)
+                  float *lout, void *ws, size_t ws_bytes, void *stream, void *ev0 = nullptr,
+                  void *ev1 = nullptr)
 {
     const int st = validate(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, ws,
                             ws_bytes);
@@ -1226,7 +1282,7 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (R * T > kMaxRows)
         return launch_rows(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, wsb,
-                           dev, s);
+                           dev, s, ev0, ev1);
     Args a;
     a.hidden = static_cast<const uint16_t *>(hidden);
     a.w = w;
@@ -1261,11 +1317,14 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "stage kernel launch");
+    const int rs = record_event(ev0, s, "event record before verify kernel");
+    if (rs != INT4VH_OK)
+        return rs;
     hipLaunchKernelGGL(fn.verify, dim3(grid), dim3(kThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "verify kernel launch");
-    return INT4VH_OK;
+    return record_event(ev1, s, "event record after verify kernel");
 }
 
 } // namespace
@@ -1311,6 +1370,18 @@ int verify_lm_head_int4_batch(const void *hidden, const uint8_t *packed_w, const
 {
     return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
                          n_accepted, logits_out, workspace, workspace_bytes, stream);
+}
+
+int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
+                                    const void *scales, const int32_t *draft_ids, int R, int T,
+                                    int V, int H, float *logits_max, int32_t *argmax_ids,
+                                    int32_t *n_accepted, float *logits_out, void *workspace,
+                                    size_t workspace_bytes, void *stream, void *event_before,
+                                    void *event_after)
+{
+    return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
+                         n_accepted, logits_out, workspace, workspace_bytes, stream, event_before,
+                         event_after);
 }
 
 int verify_lm_head_int4_check_weights(const uint8_t *packed_w, int V, int H, int32_t *n_bad_out,

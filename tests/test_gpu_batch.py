@@ -258,3 +258,30 @@ def test_batch_config_full_size(vh, orc):
     assert np.all(np.abs(g["logits_max"] - np.array(
         [g["logits"][r, i] for r, i in enumerate(g["argmax_ids"])])) == 0)
     say(f"ids differ at {differ.tolist()}, max logit error {err.max():.3g}")
+
+
+@pytest.mark.parametrize("R,T", [(1, 16), (64, 4)])
+def test_timed_entry_point(vh, orc, R, T):
+    """The instrumented call gives the same results as the plain one, and its
+    events bracket the main kernel only: a positive time, shorter than the
+    whole call."""
+    V, H = 20000, 2048
+    d = synth.uniform_inputs(R * T, V, H, seed=90 + R)
+    x = dev(d["hidden"], torch.float16).reshape(R, T, H)
+    w = dev(d["packed"])
+    s = dev(d["scales"], torch.float16)
+    dr = dev(np.zeros((R, T - 1), np.int32))
+    ws = vh.Workspace(vh.workspace_bytes(R, T, V, H), torch.device("cuda:0"))
+    say(f"timed entry point R={R} T={T}")
+    plain = vh.verify_batch(x, w, s, dr, logits=True, workspace=ws)
+    torch.cuda.synchronize()
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    timed = vh.verify_batch(x, w, s, dr, logits=True, workspace=ws, events=(e[1], e[2]))
+    e[3].record()
+    torch.cuda.synchronize()
+    for a, b in zip(plain, timed):
+        assert torch.equal(a, b)
+    t_kernel = e[1].elapsed_time(e[2])
+    t_call = e[0].elapsed_time(e[3])
+    assert 0 < t_kernel <= t_call
