@@ -165,6 +165,9 @@ __device__ __forceinline__ void load_xs16(const uint16_t *hrow, const uint16_t *
     const u32x4 *sp = reinterpret_cast<const u32x4 *>(scales + h0);
     u32x4 hx[2] = {hp[0], hp[1]};
     u32x4 sx[2] = {sp[0], sp[1]};
+    // all four loads in flight before the first use (left alone, the
+    // scheduler waits for one of them before issuing the others)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         uint32_t hw = hx[j >> 3][(j >> 1) & 3], sw = sx[j >> 3][(j >> 1) & 3];
