@@ -678,8 +678,9 @@ constexpr int kRVBlocks = kRVocTile / 16;               // MFMA column blocks pe
 constexpr int kRStepH = 128;                            // hidden channels per K step
 constexpr int kRStepBytes = kRVocTile * kRStepH / 2;    // packed weight bytes of one K step
 constexpr int kRTileBytes = kRVocTile * kRStepH;        // the same weights as int8 MFMA fragments
-constexpr int kRStageThreads = 256;
-constexpr int kRStageSteps = 4;                         // K steps per stage workgroup
+constexpr int kRStageSteps = 8;                         // K steps per stage workgroup
+constexpr int kRStageThreads = kRStageSteps * 2 * 64;   // one (step, half, lane) per thread
+static_assert(kRStageThreads % (16 * 64) == 0, "whole waves per token in the exponent pass");
 constexpr int kRChunks = kRStepBytes / (kRThreads * 16);   // 16-byte weight chunks per thread and step
 static_assert(kRChunks * kRWaves == kRVBlocks, "each wave stages whole column blocks");
 
@@ -737,36 +738,56 @@ __device__ __forceinline__ int key_index(unsigned long long k)
 // ---------------------------------------------------------------- stage_rows_kernel
 // Grid (token blocks of the padded tiles, groups of kRStageSteps K steps).
 // Every workgroup finds the step exponents of its 16 tokens (the largest
-// |x*s| over the whole row), then writes the fragments of its K steps.
-// Tokens >= M and channels >= H get zero codes.
+// |x*s| over the whole row: 64 threads per token, all of a thread's loads in
+// flight at once), then writes the fragments of its K steps, one
+// (step, half, lane) word triple per thread.  Tokens >= M and channels >= H
+// get zero codes.
 __global__ void __launch_bounds__(kRStageThreads) stage_rows_kernel(RArgs a)
 {
+    __shared__ float s_am[16][kRStageThreads / 16 / 64];
     __shared__ int s_e[16];
     const int tb = blockIdx.x;
     const int tid = threadIdx.x;
     const int H = a.H;
     {
-        const int n = tid >> 4, sub = tid & 15;   // 16 threads per token
+        constexpr int kPerTok = kRStageThreads / 16;           // threads per token
+        constexpr int kChunks = (INT4VH_MAX_H / 16 + kPerTok - 1) / kPerTok;
+        const int n = tid / kPerTok, sub = tid % kPerTok;
         const int tok = tb * 16 + n;
-        float am = 0.0f;
-        if (tok < a.M) {
-            const uint16_t *hrow = a.hidden + (size_t)tok * H;
-            for (int c = sub; c * 16 < H; c += 16) {
-                float xs[16];
-                load_xs16(hrow, a.scales, c * 16, xs);
+        const uint16_t *hrow = a.hidden + (size_t)(tok < a.M ? tok : 0) * H;
+        float xs[kChunks][16];
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    am = fmaxf(am, fabsf(xs[j]));
+        for (int j = 0; j < kChunks; ++j) {
+            const int c = sub + kPerTok * j;
+            if (tok < a.M && c * 16 < H) {
+                load_xs16(hrow, a.scales, c * 16, xs[j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    xs[j][i] = 0.0f;
             }
         }
+        float am = 0.0f;
 #pragma unroll
-        for (int off = 8; off >= 1; off >>= 1)
+        for (int j = 0; j < kChunks; ++j)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                am = fmaxf(am, fabsf(xs[j][i]));
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
             am = fmaxf(am, __shfl_xor(am, off));
-        if (sub == 0) {
-            const int e = code_exponent(am);
-            s_e[n] = e;
+        if ((tid & 63) == 0)
+            s_am[n][sub / 64] = am;
+        __syncthreads();
+        if (tid < 16) {
+            float m = s_am[tid][0];
+#pragma unroll
+            for (int w = 1; w < kPerTok / 64; ++w)
+                m = fmaxf(m, s_am[tid][w]);
+            const int e = code_exponent(m);
+            s_e[tid] = e;
             if (blockIdx.y == 0)
-                a.exps[tb * 16 + n] = e;
+                a.exps[tb * 16 + tid] = e;
         }
     }
     __syncthreads();
@@ -775,28 +796,26 @@ __global__ void __launch_bounds__(kRStageThreads) stage_rows_kernel(RArgs a)
     const bool live = tok < a.M;
     const uint16_t *hrow = a.hidden + (size_t)(live ? tok : 0) * H;
     const int e = s_e[n16];
-    const int s0 = blockIdx.y * kRStageSteps;
-    for (int p = tid >> 6; p < 2 * kRStageSteps; p += kRStageThreads / 64) {
-        const int s = s0 + (p >> 1), h = p & 1;
-        if (s >= a.n_steps)
-            break;
-        // lane group grp, half h: channels 32*grp + 16*h .. +15 of the step
-        const int ch0 = s * kRStepH + 32 * grp + 16 * h;
-        float xs[16];
-        if (live && ch0 < H) {
-            load_xs16(hrow, a.scales, ch0, xs);
-        } else {
+    const int p = tid >> 6;                                  // (step, half) pair of this thread
+    const int s = blockIdx.y * kRStageSteps + (p >> 1), h = p & 1;
+    if (s >= a.n_steps)
+        return;
+    // lane group grp, half h: channels 32*grp + 16*h .. +15 of the step
+    const int ch0 = s * kRStepH + 32 * grp + 16 * h;
+    float xs[16];
+    if (live && ch0 < H) {
+        load_xs16(hrow, a.scales, ch0, xs);
+    } else {
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                xs[j] = 0.0f;
-        }
-        uint32_t limbw[3][4];
-        split_limbs(xs, e, limbw);
-#pragma unroll
-        for (int l = 0; l < 3; ++l)
-            a.frag_out[rfrag_index(tb, a.n_steps, s, h, l, L)] =
-                u32x4{limbw[l][0], limbw[l][1], limbw[l][2], limbw[l][3]};
+        for (int j = 0; j < 16; ++j)
+            xs[j] = 0.0f;
     }
+    uint32_t limbw[3][4];
+    split_limbs(xs, e, limbw);
+#pragma unroll
+    for (int l = 0; l < 3; ++l)
+        a.frag_out[rfrag_index(tb, a.n_steps, s, h, l, L)] =
+            u32x4{limbw[l][0], limbw[l][1], limbw[l][2], limbw[l][3]};
 }
 
 // ---------------------------------------------------------------- verify_rows_kernel
@@ -816,7 +835,14 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
     const int lane = tid & 63, wave = tid >> 6;
     const int n16 = lane & 15;   // MFMA row of A / column of B and D
     const int grp = lane >> 4;   // 16-lane group: K sub-block, D rows 4*grp..4*grp+3
-    const int G = gridDim.x, b = blockIdx.x;
+    const int G = gridDim.x;
+    // Item order: workgroups are dispatched to the 8 XCDs round-robin, so
+    // blockIdx b runs on XCD b % 8.  Renumbering b -> (b % 8) * (G / 8) + b / 8
+    // gives neighbouring item numbers -- the token tiles of one vocabulary
+    // tile -- to workgroups of the same XCD, which then read that tile's
+    // weights at the same time through one L2.
+    const int b = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8)
+                               : (int)blockIdx.x;
     const int n_steps = a.n_steps, n_mt = a.n_mt;
     const int n_my = b < a.n_items ? (a.n_items - 1 - b) / G + 1 : 0;
 
