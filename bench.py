@@ -60,6 +60,32 @@ def cpu_baseline(cfg, head, trials, n_threads):
                        f"{cfg.V} vocab rows), trial seeds {list(trials)}")
 
 
+# HBM bytes per launch of the main kernel, from two rocprofv3 runs (FETCH_SIZE,
+# then WRITE_SIZE) scaled by what the same counters read for a device copy of
+# known size (factors 2.000 and 1.000); the summaries are in profiles/.  Each
+# entry holds the SHA-256 of the kernel source it was measured on: once the
+# source changes the entry no longer applies and `traffic` is null.
+MEASURED_TRAFFIC = {
+    "full_t16": dict(read=391_094_067, write=73_933,
+                     source_sha256="417cc79d8d67931dc0ed1fe3c72bbfff43f004c45622ea1dac443c7b01f7833f"),
+    "batch": dict(read=684_024_422, write=9_736_499,
+                  source_sha256="417cc79d8d67931dc0ed1fe3c72bbfff43f004c45622ea1dac443c7b01f7833f"),
+}
+
+
+def measured_traffic(cfg, t_launch):
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(cfg.name)
+    if rec is None:
+        return None, None
+    src = os.path.join(ROOT, "int4_output_head_amd", "csrc", "int4vh.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None, None
+    nbytes = rec["read"] + rec["write"]
+    return round(nbytes / t_launch / 1e9, 2), nbytes
+
+
 def roofline(cfg, t_launch, gbs):
     """Roofline of the dominant (main verify) kernel, t_launch being its mean
     duration between HIP events recorded right around it.  Up to 16 rows the
@@ -67,13 +93,16 @@ def roofline(cfg, t_launch, gbs):
     int8 MFMAs do: algorithmic work is one multiply-add per (row, vocabulary
     row, channel), 2*M*V*H int8 ops; the kernel executes three times that
     (three limbs per activation code), reported beside it."""
+    traffic, traffic_bytes = measured_traffic(cfg, t_launch)
     if cfg.M <= SINGLE_BLOCK_ROWS:
         return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "traffic_bytes_per_launch": traffic_bytes}
     ops = 2.0 * cfg.M * cfg.V * cfg.H
     tops = ops / t_launch / 1e12
     return {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-            "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": None,
+            "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
+            "traffic_unit": "GB/s", "traffic_bytes_per_launch": traffic_bytes,
             "executed_int8_tops": round(3 * tops, 2),
             "executed_frac": round(3 * tops / INT8_PEAK_TOPS, 4),
             "weight_gb_s": round(gbs, 2)}
