@@ -108,6 +108,101 @@ def roofline(cfg, t_launch, gbs):
             "weight_gb_s": round(gbs, 2)}
 
 
+REQUANT = dict(V=151936, H=5120, N=4096)
+
+
+def bench_requant(args):
+    """The offline requantisation of the full-vocabulary head (V=151936,
+    H=5120, binary16 weights, 4096 binary16 calibration rows): one step is
+    the whole tool (calibration maxima, scales, quantise + pack).  The pack
+    kernel dominates; its roofline counts the bytes it must move: the
+    binary16 head read once, the packed head written once, the scales."""
+    import torch
+    from int4_output_head_amd import binding, synth
+
+    V, H, N = REQUANT["V"], REQUANT["H"], REQUANT["N"]
+    dev = torch.device("cuda:0")
+    binding.load_library()
+    t0 = time.time()
+    inp = synth.requant_inputs(V, H, N, seed=0)
+    log(f"requant inputs generated in {time.time() - t0:.1f}s")
+    W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.float16).to(dev)
+    acts = torch.from_numpy(inp["acts"].view(np.int16)).view(torch.float16).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # parity gate: scales and 256 sampled packed rows against the oracle
+    from oracle import requant as rq
+    packed, scales, _ = binding.requantize(W, acts)
+    torch.cuda.synchronize()
+    s_want = rq.scales_from_amax(rq.calib_amax(inp["acts"], rq.F16))
+    rows = np.sort(np.random.default_rng(0).choice(V, 256, replace=False))
+    got_rows = packed[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    gate = dict(scales_equal=bool(np.array_equal(scales.cpu().view(torch.int16).numpy().view(np.uint16),
+                                                 s_want)),
+                rows_checked=int(rows.size),
+                rows_equal=int(np.sum(np.all(got_rows == rq.pack(rq.quantize(inp["W"][rows], rq.F16, s_want)),
+                                              axis=1))))
+    log(f"parity gate: {gate}")
+
+    t_w = time.time()
+    i = 0
+    while i < args.warmup or time.time() - t_w < 0.5:
+        binding.requantize(W, acts)
+        i += 1
+    torch.cuda.synchronize()
+    steps = args.steps
+    k0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    k1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    amax = torch.empty(H, dtype=torch.float32, device=dev)
+    b0.record(stream)
+    for i in range(steps):
+        binding.requant_amax(acts, amax)
+        sc = binding.requant_scales(amax)
+        binding.requant_pack(W, sc, events=(k0[i], k1[i]))
+    b1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = b0.elapsed_time(b1) / steps
+    per_k = np.array([a.elapsed_time(b) for a, b in zip(k0, k1)])
+    t_launch = float(per_k.mean()) * 1e-3
+    pack_bytes = V * H * 2 + V * H // 2 + H * 2
+    step_bytes = pack_bytes + N * H * 2
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = pack_bytes / t_launch / 1e9
+    result = {
+        "metric": "int4 lm_head requantisation: HBM GB/s of the whole offline step",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"requantise + pack the full-vocab head V={V} H={H} binary16 "
+                               f"with {N} binary16 calibration rows",
+                   "V": V, "H": H, "N": N, "timing": "eager, HIP events around the whole step"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "pack_kernel_us": {"mean": round(per_k.mean() * 1e3, 3),
+                           "p10": round(np.percentile(per_k, 10) * 1e3, 3),
+                           "p50": round(np.percentile(per_k, 50) * 1e3, 3),
+                           "p90": round(np.percentile(per_k, 90) * 1e3, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": pack_bytes},
+        "parity_gate": gate,
+    }
+    if not args.no_cpu_baseline:
+        n_rows = 8192
+        t0 = time.time()
+        s16 = rq.scales_from_amax(rq.calib_amax(inp["acts"], rq.F16))
+        rq.pack(rq.quantize(inp["W"][:n_rows], rq.F16, s16))
+        t = time.time() - t0
+        nbytes = n_rows * H * 2 + n_rows * H // 2 + H * 2 + N * H * 2
+        result["cpu_baseline"] = {
+            "value": round(nbytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"the oracle's calibration maxima over all {N} rows, scales, and "
+                      f"quantise + pack of the first {n_rows} of {V} head rows (numpy, one thread)"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +220,10 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path runs on a single MI355X; see the sharding notes)", file=sys.stderr)
         sys.exit(2)
+
+    if args.config == "requant":
+        bench_requant(args)
+        return
 
     import torch
     from int4_output_head_amd import binding, synth

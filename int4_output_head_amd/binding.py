@@ -51,6 +51,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.verify_lm_head_int4_status_string.restype = ctypes.c_char_p
         L.verify_lm_head_int4_last_error.argtypes = []
         L.verify_lm_head_int4_last_error.restype = ctypes.c_char_p
+        # offline requantisation (include/int4vh_requant.h)
+        L.requant_lm_head_int4_amax.argtypes = [P, i32, i32, i32, P, i32, P]
+        L.requant_lm_head_int4_amax.restype = i32
+        L.requant_lm_head_int4_scales.argtypes = [P, i32, P, P]
+        L.requant_lm_head_int4_scales.restype = i32
+        L.requant_lm_head_int4_pack.argtypes = [P, i32, i32, i32, P, P, P]
+        L.requant_lm_head_int4_pack.restype = i32
+        L.requant_lm_head_int4_pack_timed.argtypes = [P, i32, i32, i32, P, P, P, P, P]
+        L.requant_lm_head_int4_pack_timed.restype = i32
+        L.requant_lm_head_int4.argtypes = [P, i32, i32, i32, P, i32, i32, P, P, P, P]
+        L.requant_lm_head_int4.restype = i32
         _lib = L
         return L
 
@@ -223,3 +234,102 @@ def check_weights(packed_w) -> torch.Tensor:
     if st != OK:
         _raise(st, "check_weights")
     return out
+
+
+# ---------------------------------------------------------------- requantisation
+
+F16, BF16 = 0, 1
+_DTYPES = {torch.float16: F16, torch.bfloat16: BF16}
+
+
+def _dtype_code(t, name):
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"{name} must be float16 or bfloat16, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def requant_amax(acts, amax=None, *, accumulate: bool = False) -> torch.Tensor:
+    """Per-channel max |acts| of calibration rows acts [N, H] (float16 or
+    bfloat16) into amax (float32 [H]); with accumulate=True the running
+    maximum of an existing amax.  Returns amax (asynchronous)."""
+    if not isinstance(acts, torch.Tensor) or not acts.is_cuda:
+        raise TypeError("acts must be a CUDA (HIP) tensor")
+    dt = _dtype_code(acts, "acts")
+    _check(acts, "acts", acts.dtype, 2)
+    N, H = acts.shape
+    if amax is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs an existing amax")
+        amax = torch.empty(H, dtype=torch.float32, device=acts.device)
+    _check(amax, "amax", torch.float32, 1)
+    if amax.shape[0] != H:
+        raise ValueError("amax must hold H values")
+    st = load_library().requant_lm_head_int4_amax(_ptr(acts), dt, N, H, _ptr(amax), int(accumulate),
+                                                  _stream_ptr(acts.device))
+    if st != OK:
+        _raise(st, "requant_lm_head_int4_amax")
+    return amax
+
+
+def requant_scales(amax) -> torch.Tensor:
+    """float16 scales [H] = amax / 7 (binary32 division, rounded to binary16)."""
+    _check(amax, "amax", torch.float32, 1)
+    H = amax.shape[0]
+    scales = torch.empty(H, dtype=torch.float16, device=amax.device)
+    st = load_library().requant_lm_head_int4_scales(_ptr(amax), H, _ptr(scales),
+                                                    _stream_ptr(amax.device))
+    if st != OK:
+        _raise(st, "requant_lm_head_int4_scales")
+    return scales
+
+
+def requant_pack(W, scales, *, events=None) -> torch.Tensor:
+    """Quantise the head W [V, H] (float16 or bfloat16) with per-channel
+    scales (float16 [H]) and pack it: uint8 [V, H/2] in the verify layout.
+    events=(before, after) are recorded right around the pack kernel."""
+    if not isinstance(W, torch.Tensor) or not W.is_cuda:
+        raise TypeError("W must be a CUDA (HIP) tensor")
+    dt = _dtype_code(W, "W")
+    _check(W, "W", W.dtype, 2)
+    _check(scales, "scales", torch.float16, 1)
+    V, H = W.shape
+    if scales.shape[0] != H:
+        raise ValueError("scales must hold H values")
+    packed = torch.empty((V, H // 2), dtype=torch.uint8, device=W.device)
+    L = load_library()
+    if events is None:
+        st = L.requant_lm_head_int4_pack(_ptr(W), dt, V, H, _ptr(scales), _ptr(packed),
+                                         _stream_ptr(W.device))
+    else:
+        stream = torch.cuda.current_stream(W.device)
+        st = L.requant_lm_head_int4_pack_timed(_ptr(W), dt, V, H, _ptr(scales), _ptr(packed),
+                                               _stream_ptr(W.device),
+                                               _event_handle(events[0], stream),
+                                               _event_handle(events[1], stream))
+    if st != OK:
+        _raise(st, "requant_lm_head_int4_pack")
+    return packed
+
+
+def requantize(W, acts):
+    """The whole offline step for one calibration batch: returns (packed
+    uint8 [V, H/2], scales float16 [H], amax float32 [H])."""
+    for t, n in ((W, "W"), (acts, "acts")):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise TypeError(f"{n} must be a CUDA (HIP) tensor")
+    wdt, adt = _dtype_code(W, "W"), _dtype_code(acts, "acts")
+    _check(W, "W", W.dtype, 2)
+    _check(acts, "acts", acts.dtype, 2)
+    V, H = W.shape
+    N = acts.shape[0]
+    if acts.shape[1] != H:
+        raise ValueError("acts and W must have the same H")
+    dev = W.device
+    amax = torch.empty(H, dtype=torch.float32, device=dev)
+    scales = torch.empty(H, dtype=torch.float16, device=dev)
+    packed = torch.empty((V, H // 2), dtype=torch.uint8, device=dev)
+    st = load_library().requant_lm_head_int4(_ptr(W), wdt, V, H, _ptr(acts), adt, N, _ptr(amax),
+                                             _ptr(scales), _ptr(packed), _stream_ptr(dev))
+    if st != OK:
+        _raise(st, "requant_lm_head_int4")
+    return packed, scales, amax

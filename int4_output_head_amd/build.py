@@ -6,7 +6,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "int4vh.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("int4vh.hip", "requant.hip")]
 OUT = os.path.join(HERE, "libint4vh.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -20,7 +20,7 @@ HIPCC_FLAGS = [
 def build_library(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = OUT + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

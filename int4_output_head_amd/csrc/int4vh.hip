@@ -47,6 +47,38 @@
 #include <string>
 
 #include "int4vh.h"
+#include "int4vh_internal.h"
+
+namespace int4vh_detail {
+
+thread_local std::string g_last_error;
+
+int hip_fail(hipError_t e, const char *what)
+{
+    g_last_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
+    return INT4VH_EHIP;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices];
+std::once_flag g_cu_once[kMaxDevices];
+} // namespace
+
+int cu_count(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices)
+        return 256;
+    std::call_once(g_cu_once[dev], [dev] {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        g_cu_count[dev] = n;
+    });
+    return g_cu_count[dev];
+}
+
+} // namespace int4vh_detail
 
 namespace {
 
@@ -1112,30 +1144,12 @@ __global__ void __launch_bounds__(256) count_bad_nibbles(const u32x4 *w, size_t 
 
 // ---------------------------------------------------------------- host side
 
-thread_local std::string g_last_error;
-
 int hip_fail(hipError_t e, const char *what)
 {
-    g_last_error = std::string(what) + ": " + hipGetErrorName(e) + " (" + hipGetErrorString(e) + ")";
-    return INT4VH_EHIP;
+    return int4vh_detail::hip_fail(e, what);
 }
 
-constexpr int kMaxDevices = 64;
-int g_cu_count[kMaxDevices];
-std::once_flag g_cu_once[kMaxDevices];
-
-int cu_count(int dev)
-{
-    if (dev < 0 || dev >= kMaxDevices)
-        return 256;
-    std::call_once(g_cu_once[dev], [dev] {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        g_cu_count[dev] = n;
-    });
-    return g_cu_count[dev];
-}
+using int4vh_detail::cu_count;
 
 bool aligned(const void *p, size_t al)
 {
@@ -1452,7 +1466,7 @@ const char *verify_lm_head_int4_status_string(int status)
 
 const char *verify_lm_head_int4_last_error(void)
 {
-    return g_last_error.c_str();
+    return int4vh_detail::g_last_error.c_str();
 }
 
 } // extern "C"

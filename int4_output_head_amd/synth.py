@@ -233,3 +233,33 @@ def uniform_inputs(M: int, V: int, H: int, seed: int, heavy_frac: float = 0.0) -
     s = f16_bits(rng.lognormal(-4.0, 0.5, size=H))
     x = f16_bits(rng.standard_normal((M, H)))
     return dict(q=q, packed=pack_int4(q), hidden=x, scales=s)
+
+
+# ---------------------------------------------------------------- requantisation inputs
+
+def bf16_bits(a) -> np.ndarray:
+    """float64 values -> bfloat16 bit patterns (binary32 rounding to nearest
+    even first, then the upper half rounded to nearest even)."""
+    f = np.asarray(a, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (f + 0x7FFF + ((f >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def requant_inputs(V: int, H: int, N: int, seed: int, w_dtype: str = "f16",
+                   a_dtype: str = "f16") -> dict:
+    """A synthetic full-precision head W [V, H] and N calibration rows of
+    final hidden states [N, H], as bit patterns of ``w_dtype`` / ``a_dtype``
+    ("f16" or "bf16").  No checkpoint or calibration set is available, so
+    both are drawn: channel magnitudes c[h] ~ lognormal(0, 1) (a few channels
+    carry much larger activations than the rest), activations N(0, 1) * c[h],
+    weights N(0, 1) * 2 * c[h], so that weight / (largest activation / 7)
+    spreads over about +-8 and a few per cent of the codes clamp."""
+    rng = _rng(5, seed)
+    c = rng.lognormal(0.0, 1.0, size=H)
+    acts = rng.standard_normal((N, H)) * c
+    W = np.empty((V, H), np.float64)
+    for r0 in range(0, V, 8192):
+        r1 = min(V, r0 + 8192)
+        W[r0:r1] = rng.standard_normal((r1 - r0, H)) * (2.0 * c)
+    enc = {"f16": f16_bits, "bf16": bf16_bits}
+    return dict(W=enc[w_dtype](W), acts=enc[a_dtype](acts))

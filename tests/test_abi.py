@@ -8,16 +8,20 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "int4vh.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 LIB = os.path.join(ROOT, "int4_output_head_amd", "libint4vh.so")
 
 OK, EINVAL, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(verify_lm_head_int4\w*)\s*\(", text)))
+    """Every function declared by the public headers (comments stripped)."""
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w ]*?[\s*]+(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -41,8 +45,13 @@ def lib():
 
 def test_header_declares_expected_api():
     names = declared_functions()
-    assert "verify_lm_head_int4" in names and "verify_lm_head_int4_batch" in names
-    assert len(names) >= 7
+    for n in ("verify_lm_head_int4", "verify_lm_head_int4_batch", "verify_lm_head_int4_batch_timed",
+              "verify_lm_head_int4_workspace_bytes", "verify_lm_head_int4_workspace_init",
+              "verify_lm_head_int4_check_weights", "verify_lm_head_int4_status_string",
+              "verify_lm_head_int4_last_error", "requant_lm_head_int4_amax",
+              "requant_lm_head_int4_scales", "requant_lm_head_int4_pack",
+              "requant_lm_head_int4_pack_timed", "requant_lm_head_int4"):
+        assert n in names, n
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -141,3 +150,41 @@ def test_workspace_init_and_check_weights_validation(lib):
     assert lib.verify_lm_head_int4_check_weights(None, 10, 64, P(A), None) == EINVAL
     assert lib.verify_lm_head_int4_check_weights(P(A), 10, 48, P(A), None) == EINVAL
     assert lib.verify_lm_head_int4_check_weights(P(A + 8), 10, 64, P(A), None) == EALIGN
+
+
+def test_requant_rejects_invalid_arguments(lib):
+    """Host validation of the requantisation entry points (fake pointers,
+    nothing launched)."""
+    P, i32 = ctypes.c_void_p, ctypes.c_int
+    am = lib.requant_lm_head_int4_amax
+    am.argtypes = [P, i32, i32, i32, P, i32, P]
+    sc = lib.requant_lm_head_int4_scales
+    sc.argtypes = [P, i32, P, P]
+    pk = lib.requant_lm_head_int4_pack
+    pk.argtypes = [P, i32, i32, i32, P, P, P]
+    rq = lib.requant_lm_head_int4
+    rq.argtypes = [P, i32, i32, i32, P, i32, i32, P, P, P, P]
+    a = P(A)
+    assert am(None, 0, 4, 64, a, 0, None) == EINVAL
+    assert am(a, 2, 4, 64, a, 0, None) == EINVAL          # unknown dtype
+    assert am(a, 0, 0, 64, a, 0, None) == EINVAL
+    assert am(a, 0, 4, 48, a, 0, None) == EINVAL
+    assert am(a, 1, 4, 64, None, 0, None) == EINVAL
+    assert am(P(A + 8), 0, 4, 64, a, 0, None) == EALIGN
+    assert am(a, 0, 4, 64, P(A + 2), 0, None) == EALIGN
+    assert am(a, 0, 1 << 30, 4096, a, 0, None) == EUNSUPPORTED
+    assert sc(None, 64, a, None) == EINVAL
+    assert sc(a, 16, a, None) == EINVAL
+    assert sc(a, 64, P(A + 2), None) == EALIGN
+    assert pk(a, 0, 0, 64, a, a, None) == EINVAL
+    assert pk(a, 3, 10, 64, a, a, None) == EINVAL
+    assert pk(a, 0, 10, 40, a, a, None) == EINVAL
+    assert pk(a, 0, 10, 64, None, a, None) == EINVAL
+    assert pk(a, 0, 10, 64, a, None, None) == EINVAL
+    assert pk(P(A + 2), 0, 10, 64, a, a, None) == EALIGN
+    assert pk(a, 0, 10, 64, a, P(A + 8), None) == EALIGN
+    assert pk(a, 0, 1 << 28, 8192, a, a, None) == EUNSUPPORTED
+    assert rq(a, 0, 10, 64, a, 0, 0, a, a, a, None) == EINVAL
+    assert rq(a, 0, 10, 64, a, 5, 4, a, a, a, None) == EINVAL
+    assert rq(a, 0, 10, 64, a, 0, 4, a, P(A + 2), a, None) == EALIGN
+    assert rq(a, 0, 1 << 28, 8192, a, 0, 4, a, a, a, None) == EUNSUPPORTED
