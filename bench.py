@@ -274,7 +274,18 @@ def main():
     work = binding.Workspace(binding.workspace_bytes(cfg.R, cfg.T, cfg.V, cfg.H), dev)
     stream = torch.cuda.current_stream(dev)
 
+    # The draft-vocabulary head: its rows are a subset of the full vocabulary
+    # (a sorted random subset of 151936 token ids), and the step reports
+    # token ids through the row -> token map.
+    vmap_np = None
+    if cfg.name == "draft_vocab":
+        vmap_np = np.sort(np.random.default_rng(0).choice(151936, cfg.V, replace=False)).astype(np.int32)
+        vmap = torch.from_numpy(vmap_np).to(dev)
+
     def step(i):
+        if vmap_np is not None:
+            return binding.verify_mapped(xs[i % n_trials], ws[i % copies], s, vmap, ds[i % n_trials],
+                                         workspace=work)
         return binding.verify_batch(xs[i % n_trials], ws[i % copies], s, ds[i % n_trials],
                                     workspace=work)
 
@@ -284,6 +295,8 @@ def main():
         lmax, amax, nacc = step(trial)
         if ref_ids[trial] is not None:
             g = amax.cpu().numpy()
+            if vmap_np is not None:
+                g = np.searchsorted(vmap_np, g)          # token ids back to head rows
             gate["rows"] += cfg.M
             gate["ids_equal"] += int(np.sum(g == ref_ids[trial]))
             gaps = np.array(stored["trials"][str(trial)]["gap"])
@@ -391,6 +404,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.desc, "V": cfg.V, "H": cfg.H, "R": cfg.R, "T": cfg.T,
                    "head_copies_rotated": copies, "trials": n_trials,
+                   **({"vocab_map": f"rows map to a sorted random {cfg.V} of 151936 token ids"}
+                      if vmap_np is not None else {}),
                    "timing": f"HIP graph of {calls_per_graph} steps replayed {replays}x "
                              f"after {n_warm} untimed replays"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

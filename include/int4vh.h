@@ -147,6 +147,33 @@ int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
                                     size_t workspace_bytes, void *stream, void *event_before,
                                     void *event_after);
 
+/* A head whose rows are a subset of the vocabulary: the draft vocabulary of
+ * "HyperQwen: 1,000 tok/s on a Single RTX 3090 Through Aggressive
+ * Recurrent-State Speculation", Technical Insight (speculation configuration:
+ * the drafter's vocabulary is cut to the 8192 tokens actually observed, out of
+ * about 152k), and the 40k-token draft vocabulary of the HyperQwen README
+ * ("Roadmap").  vocab_ids (device int32 [V], required) gives the token id of
+ * each head row and must be strictly increasing and non-negative (checked by
+ * verify_lm_head_int4_check_vocab_map, not by this call).  The argmax is taken
+ * over the head's rows exactly as in verify_lm_head_int4_batch (the lowest row
+ * wins ties, which is the lowest token id for an increasing map); argmax_ids
+ * then holds vocab_ids[row], and the drafts are compared with those token ids.
+ * logits_out, when given, is indexed by head row.  Other arguments, results
+ * and errors as verify_lm_head_int4_batch; INT4VH_EINVAL if vocab_ids is NULL,
+ * INT4VH_EALIGN if it is not 4-byte aligned. */
+int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, const void *scales,
+                               const int32_t *vocab_ids, const int32_t *draft_ids, int R, int T,
+                               int V, int H, float *logits_max, int32_t *argmax_ids,
+                               int32_t *n_accepted, float *logits_out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Count the positions i of a row -> token map (device int32 [V]) where it is
+ * not strictly increasing and non-negative (vocab_ids[0] < 0, or
+ * vocab_ids[i] <= vocab_ids[i-1]) into *n_bad_out (device int32,
+ * overwritten).  Asynchronous on `stream`. */
+int verify_lm_head_int4_check_vocab_map(const int32_t *vocab_ids, int V, int32_t *n_bad_out,
+                                        void *stream);
+
 /* Count illegal nibbles (0x8) of a packed head into *n_bad_out (device int32,
  * overwritten).  Asynchronous on `stream`. */
 int verify_lm_head_int4_check_weights(const uint8_t *packed_w, int V, int H,

@@ -51,6 +51,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.verify_lm_head_int4_status_string.restype = ctypes.c_char_p
         L.verify_lm_head_int4_last_error.argtypes = []
         L.verify_lm_head_int4_last_error.restype = ctypes.c_char_p
+        L.verify_lm_head_int4_mapped.argtypes = [P, P, P, P, P, i32, i32, i32, i32, P, P, P, P,
+                                                 P, sz, P]
+        L.verify_lm_head_int4_mapped.restype = i32
+        L.verify_lm_head_int4_check_vocab_map.argtypes = [P, i32, P, P]
+        L.verify_lm_head_int4_check_vocab_map.restype = i32
         # offline requantisation (include/int4vh_requant.h)
         L.requant_lm_head_int4_amax.argtypes = [P, i32, i32, i32, P, i32, P]
         L.requant_lm_head_int4_amax.restype = i32
@@ -183,6 +188,68 @@ def verify_batch(hidden, packed_w, scales, draft_ids=None, *, R: int | None = No
     if st != OK:
         _raise(st, "verify_lm_head_int4_batch")
     return (lmax, amax, nacc, lout) if logits else (lmax, amax, nacc)
+
+
+def verify_mapped(hidden, packed_w, scales, vocab_ids, draft_ids=None, *, R: int | None = None,
+                  logits: bool = False, workspace: Workspace | None = None):
+    """Verify through a head whose rows are a subset of the vocabulary:
+    vocab_ids (int32 [V], strictly increasing) maps each head row to its
+    token id; argmax_ids are token ids and draft_ids are compared with them.
+    Otherwise as verify_batch (hidden [R, T, H], or [R*T, H] with R)."""
+    if hidden.dim() == 3:
+        R, T, H = hidden.shape
+        hidden = hidden.reshape(R * T, H)
+    else:
+        if R is None:
+            raise ValueError("R is required for a 2-D hidden tensor")
+        T = hidden.shape[0] // R
+        H = hidden.shape[1]
+    _check(hidden, "hidden", torch.float16, 2)
+    _check(packed_w, "packed_w", torch.uint8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    _check(vocab_ids, "vocab_ids", torch.int32, 1)
+    V = packed_w.shape[0]
+    if packed_w.shape[1] * 2 != H or scales.shape[0] != H or hidden.shape[0] != R * T:
+        raise ValueError("shape mismatch between hidden, packed_w and scales")
+    if vocab_ids.shape[0] != V:
+        raise ValueError("vocab_ids must hold one id per head row")
+    dev = hidden.device
+    if T > 1:
+        if draft_ids is None:
+            raise ValueError("draft_ids is required when T > 1")
+        _check(draft_ids, "draft_ids", torch.int32)
+        if draft_ids.numel() != R * (T - 1):
+            raise ValueError("draft_ids must hold R*(T-1) ids")
+    else:
+        draft_ids = None
+    M = R * T
+    lmax = torch.empty(M, dtype=torch.float32, device=dev)
+    amax = torch.empty(M, dtype=torch.int32, device=dev)
+    nacc = torch.empty(R, dtype=torch.int32, device=dev)
+    lout = torch.empty((M, V), dtype=torch.float32, device=dev) if logits else None
+    L = load_library()
+    need = L.verify_lm_head_int4_workspace_bytes(R, T, V, H)
+    if need == 0:
+        _raise(EINVAL, "verify_mapped")
+    ws = workspace if workspace is not None else _default_workspace(dev, need)
+    st = L.verify_lm_head_int4_mapped(_ptr(hidden), _ptr(packed_w), _ptr(scales), _ptr(vocab_ids),
+                                      _ptr(draft_ids), R, T, V, H, _ptr(lmax), _ptr(amax), _ptr(nacc),
+                                      _ptr(lout), _ptr(ws.tensor), ws.nbytes, _stream_ptr(dev))
+    if st != OK:
+        _raise(st, "verify_lm_head_int4_mapped")
+    return (lmax, amax, nacc, lout) if logits else (lmax, amax, nacc)
+
+
+def check_vocab_map(vocab_ids) -> torch.Tensor:
+    """Number of positions where vocab_ids is not strictly increasing and
+    non-negative, as an int32 [1] device tensor (asynchronous)."""
+    _check(vocab_ids, "vocab_ids", torch.int32, 1)
+    out = torch.empty(1, dtype=torch.int32, device=vocab_ids.device)
+    st = load_library().verify_lm_head_int4_check_vocab_map(
+        _ptr(vocab_ids), vocab_ids.shape[0], _ptr(out), _stream_ptr(vocab_ids.device))
+    if st != OK:
+        _raise(st, "check_vocab_map")
+    return out
 
 
 def verify(hidden, packed_w, scales, draft_ids=None, *, logits: bool = False,

@@ -161,6 +161,7 @@ struct Args {
     int32_t *argmax;          // [M]
     int32_t *n_acc;           // [R]
     float *logits_out;        // [M, V] or null
+    const int32_t *vmap;      // [V] token id of each head row, or null (identity)
     uint64_t *part;           // [grid, M] packed (index << 32 | value bits)
     uint32_t *ticket;
     int32_t *exps;            // [16]
@@ -643,9 +644,10 @@ verify_kernel(Args a)
                 v0 = fv[w];
                 i0 = fi[w];
             }
+        const int id = a.vmap ? a.vmap[i0] : i0;    // row -> token id
         a.logits_max[m] = v0;
-        a.argmax[m] = i0;
-        s_arg[m] = i0;
+        a.argmax[m] = id;
+        s_arg[m] = id;
     }
     __syncthreads();
     if (threadIdx.x < (unsigned)a.R) {
@@ -725,6 +727,7 @@ struct RArgs {
     int32_t *argmax;          // [M]
     int32_t *n_acc;           // [R]
     float *logits_out;        // [M, V] or null
+    const int32_t *vmap;      // [V] token id of each head row, or null (identity)
     unsigned long long *keys; // [M] per-token winner keys, zero between calls
     uint32_t *ticket;
     int32_t *exps;            // [n_mt * 128] step exponents
@@ -1090,7 +1093,8 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
     for (int j = 0; j < kPer; ++j) {
         const int m = tid + j * kRThreads;
         if (m < M) {
-            const int idx = key_index(key[j]);
+            const int row = key_index(key[j]);
+            const int idx = a.vmap ? a.vmap[row] : row;   // row -> token id
             a.logits_max[m] = key_value(key[j]);
             a.argmax[m] = idx;
             lds.arg[m] = idx;
@@ -1135,6 +1139,20 @@ __global__ void __launch_bounds__(256) count_bad_nibbles(const u32x4 *w, size_t 
                 cnt += ((x >> (4 * k)) & 0xFu) == 0u;
         }
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1)
+        cnt += __shfl_xor(cnt, off);
+    if ((threadIdx.x & 63) == 0 && cnt)
+        atomicAdd(out, cnt);
+}
+
+// Count positions of a row -> token map that break "strictly increasing,
+// non-negative" (map[0] < 0, or map[i] <= map[i-1]).
+__global__ void __launch_bounds__(256) count_bad_map(const int32_t *map, int V, int32_t *out)
+{
+    int cnt = 0;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < V; i += gridDim.x * blockDim.x)
+        cnt += (i == 0) ? (map[0] < 0) : (map[i] <= map[i - 1]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
         cnt += __shfl_xor(cnt, off);
@@ -1257,9 +1275,11 @@ int record_event(void *ev, hipStream_t s, const char *what)
 
 int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
                 int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
-                float *lout, char *wsb, int dev, hipStream_t s, void *ev0, void *ev1)
+                float *lout, const int32_t *vmap, char *wsb, int dev, hipStream_t s, void *ev0,
+                void *ev1)
 {
     RArgs a;
+    a.vmap = vmap;
     a.hidden = static_cast<const uint16_t *>(hidden);
     a.w = w;
     a.scales = static_cast<const uint16_t *>(scales);
@@ -1310,12 +1330,14 @@ int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const 
 int launch_verify(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
                   int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
                   float *lout, void *ws, size_t ws_bytes, void *stream, void *ev0 = nullptr,
-                  void *ev1 = nullptr)
+                  void *ev1 = nullptr, const int32_t *vmap = nullptr)
 {
     const int st = validate(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, ws,
                             ws_bytes);
     if (st != INT4VH_OK)
         return st;
+    if (vmap && !aligned(vmap, 4))
+        return INT4VH_EALIGN;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -1324,9 +1346,10 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     char *wsb = static_cast<char *>(ws);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (R * T > kMaxRows)
-        return launch_rows(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, wsb,
-                           dev, s, ev0, ev1);
+        return launch_rows(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, vmap,
+                           wsb, dev, s, ev0, ev1);
     Args a;
+    a.vmap = vmap;
     a.hidden = static_cast<const uint16_t *>(hidden);
     a.w = w;
     a.scales = static_cast<const uint16_t *>(scales);
@@ -1425,6 +1448,41 @@ int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
     return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
                          n_accepted, logits_out, workspace, workspace_bytes, stream, event_before,
                          event_after);
+}
+
+int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, const void *scales,
+                               const int32_t *vocab_ids, const int32_t *draft_ids, int R, int T,
+                               int V, int H, float *logits_max, int32_t *argmax_ids,
+                               int32_t *n_accepted, float *logits_out, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    if (!vocab_ids)
+        return INT4VH_EINVAL;
+    return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
+                         n_accepted, logits_out, workspace, workspace_bytes, stream, nullptr,
+                         nullptr, vocab_ids);
+}
+
+int verify_lm_head_int4_check_vocab_map(const int32_t *vocab_ids, int V, int32_t *n_bad_out,
+                                        void *stream)
+{
+    if (!vocab_ids || !n_bad_out || V < 1)
+        return INT4VH_EINVAL;
+    if (!aligned(vocab_ids, 4) || !aligned(n_bad_out, 4))
+        return INT4VH_EALIGN;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(fill_zero_u32, dim3(1), dim3(64), 0, s, reinterpret_cast<uint32_t *>(n_bad_out), 1);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "check_vocab_map zero launch");
+    int blocks = (V + 255) / 256;
+    if (blocks > 1024)
+        blocks = 1024;
+    hipLaunchKernelGGL(count_bad_map, dim3(blocks), dim3(256), 0, s, vocab_ids, V, n_bad_out);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "check_vocab_map launch");
+    return INT4VH_OK;
 }
 
 int verify_lm_head_int4_check_weights(const uint8_t *packed_w, int V, int H, int32_t *n_bad_out,
