@@ -73,9 +73,9 @@ MEASURED_TRAFFIC = {
 }
 
 
-def measured_traffic(cfg, t_launch):
+def measured_traffic(key, t_launch):
     import hashlib
-    rec = MEASURED_TRAFFIC.get(cfg.name)
+    rec = MEASURED_TRAFFIC.get(key)
     if rec is None:
         return None, None
     src = os.path.join(ROOT, "int4_output_head_amd", "csrc", "int4vh.hip")
@@ -86,14 +86,14 @@ def measured_traffic(cfg, t_launch):
     return round(nbytes / t_launch / 1e9, 2), nbytes
 
 
-def roofline(cfg, t_launch, gbs):
+def roofline(cfg, t_launch, gbs, key=None):
     """Roofline of the dominant (main verify) kernel, t_launch being its mean
     duration between HIP events recorded right around it.  Up to 16 rows the
     weight stream bounds it (algorithmic bytes V*H/2).  Beyond, the
     int8 MFMAs do: algorithmic work is one multiply-add per (row, vocabulary
     row, channel), 2*M*V*H int8 ops; the kernel executes three times that
     (three limbs per activation code), reported beside it."""
-    traffic, traffic_bytes = measured_traffic(cfg, t_launch)
+    traffic, traffic_bytes = measured_traffic(key or cfg.name, t_launch)
     if cfg.M <= SINGLE_BLOCK_ROWS:
         return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -212,6 +212,9 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="head copies to rotate (0: auto)")
     ap.add_argument("--cpu-trials", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="sampled verification: top-k sampling with this k (0: greedy)")
+    ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain device copy of head-sized buffers (a known "
                          "number of bytes) to scale hardware byte counters")
@@ -282,7 +285,34 @@ def main():
         vmap_np = np.sort(np.random.default_rng(0).choice(151936, cfg.V, replace=False)).astype(np.int32)
         vmap = torch.from_numpy(vmap_np).to(dev)
 
-    def step(i):
+    # Sampled verification (top-k sampling at a temperature): drafter
+    # probabilities U(0.5, 1) for the 7 model-drafted positions, 1 for the
+    # positions copied from the context, and seeded uniforms.
+    sampled = args.top_k > 0
+    if sampled and cfg.M > SINGLE_BLOCK_ROWS:
+        raise SystemExit("--top-k needs a block of at most 16 rows")
+    qs, us = [], []
+    if sampled and cfg.T > 1:
+        for trial in range(n_trials):
+            rng = np.random.default_rng(1000 + trial)
+            q = np.ones((cfg.R, cfg.T - 1), np.float32)
+            q[:, :7] = rng.uniform(0.5, 1.0, size=(cfg.R, min(7, cfg.T - 1)))
+            qs.append(torch.from_numpy(q).to(dev))
+            us.append(torch.from_numpy(rng.random((cfg.R, cfg.T - 1)).astype(np.float32)).to(dev))
+
+    def nacc_of(out):
+        return out[5] if sampled else out[2]
+
+    def step(i, events=None):
+        if sampled:
+            q = qs[i % n_trials] if qs else None
+            u = us[i % n_trials] if us else None
+            return binding.verify_sampled(xs[i % n_trials], ws[i % copies], s, ds[i % n_trials], q, u,
+                                          top_k=args.top_k, temperature=args.temperature,
+                                          workspace=work, events=events)
+        if events is not None:
+            return binding.verify_batch(xs[i % n_trials], ws[i % copies], s, ds[i % n_trials],
+                                        workspace=work, events=events)
         if vmap_np is not None:
             return binding.verify_mapped(xs[i % n_trials], ws[i % copies], s, vmap, ds[i % n_trials],
                                          workspace=work)
@@ -292,7 +322,8 @@ def main():
     # parity gate against the stored oracle argmax (ids may differ only at near ties)
     gate = dict(rows=0, ids_equal=0, near_tie_rows_allowed=0)
     for trial in range(n_trials):
-        lmax, amax, nacc = step(trial)
+        out = step(trial)
+        amax = out[1]
         if ref_ids[trial] is not None:
             g = amax.cpu().numpy()
             if vmap_np is not None:
@@ -331,8 +362,7 @@ def main():
     t_begin.record(stream)
     for i in range(args.steps):
         starts[i].record(stream)
-        binding.verify_batch(xs[i % n_trials], ws[i % copies], s, ds[i % n_trials],
-                             workspace=work, events=(k0[i], k1[i]))
+        step(i, events=(k0[i], k1[i]))
         ends[i].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
@@ -383,7 +413,7 @@ def main():
     torch.cuda.synchronize()
     graph_steps = replays * calls_per_graph
     ms_per_step = g0.elapsed_time(g1) / graph_steps
-    committed_tokens = sum(int(o[2].to(torch.int64).sum().item()) + cfg.R for o in outs) * replays
+    committed_tokens = sum(int(nacc_of(o).to(torch.int64).sum().item()) + cfg.R for o in outs) * replays
 
     t_launch = float(per_k.mean()) * 1e-3
     wbytes = cfg.weight_bytes
@@ -406,6 +436,8 @@ def main():
                    "head_copies_rotated": copies, "trials": n_trials,
                    **({"vocab_map": f"rows map to a sorted random {cfg.V} of 151936 token ids"}
                       if vmap_np is not None else {}),
+                   **({"sampling": f"top-{args.top_k} at temperature {args.temperature}"}
+                      if sampled else {}),
                    "timing": f"HIP graph of {calls_per_graph} steps replayed {replays}x "
                              f"after {n_warm} untimed replays"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -420,7 +452,8 @@ def main():
                            "p10": round(np.percentile(per_k, 10) * 1e3, 3),
                            "p50": round(np.percentile(per_k, 50) * 1e3, 3),
                            "p90": round(np.percentile(per_k, 90) * 1e3, 3)},
-        "roofline": roofline(cfg, t_launch, achieved),
+        "roofline": roofline(cfg, t_launch, achieved,
+                             key=f"{cfg.name}_top{args.top_k}" if sampled else cfg.name),
         "graph_replay_matches_eager": bool(replay_ok),
         "parity_gate": gate,
     }

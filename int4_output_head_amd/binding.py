@@ -56,6 +56,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.verify_lm_head_int4_mapped.restype = i32
         L.verify_lm_head_int4_check_vocab_map.argtypes = [P, i32, P, P]
         L.verify_lm_head_int4_check_vocab_map.restype = i32
+        L.verify_lm_head_int4_sampled.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                                  ctypes.c_float, P, P, P, P, P, P, P, sz, P]
+        L.verify_lm_head_int4_sampled.restype = i32
+        L.verify_lm_head_int4_sampled_timed.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                                        ctypes.c_float, P, P, P, P, P, P, P, sz, P,
+                                                        P, P]
+        L.verify_lm_head_int4_sampled_timed.restype = i32
         # offline requantisation (include/int4vh_requant.h)
         L.requant_lm_head_int4_amax.argtypes = [P, i32, i32, i32, P, i32, P]
         L.requant_lm_head_int4_amax.restype = i32
@@ -238,6 +245,67 @@ def verify_mapped(hidden, packed_w, scales, vocab_ids, draft_ids=None, *, R: int
     if st != OK:
         _raise(st, "verify_lm_head_int4_mapped")
     return (lmax, amax, nacc, lout) if logits else (lmax, amax, nacc)
+
+
+def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, uniforms=None, *,
+                   top_k: int, temperature: float = 1.0, R: int | None = None,
+                   workspace: Workspace | None = None, events=None):
+    """Sampled verification (top-k sampling at a temperature) for R*T <= 16
+    rows.  hidden: float16 [R, T, H] (or [R*T, H] with R); draft_ids int32,
+    draft_probs and uniforms float32, each [R, T-1] (None when T == 1).
+    Returns (logits_max [R*T], argmax_ids [R*T], topk_ids [R*T, k],
+    topk_logits [R*T, k], p_draft [R, T-1], n_accepted [R]).  events=(before,
+    after) are recorded right around the main verify kernel."""
+    if hidden.dim() == 3:
+        R, T, H = hidden.shape
+        hidden = hidden.reshape(R * T, H)
+    else:
+        if R is None:
+            raise ValueError("R is required for a 2-D hidden tensor")
+        T = hidden.shape[0] // R
+        H = hidden.shape[1]
+    _check(hidden, "hidden", torch.float16, 2)
+    _check(packed_w, "packed_w", torch.uint8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    V = packed_w.shape[0]
+    if packed_w.shape[1] * 2 != H or scales.shape[0] != H or hidden.shape[0] != R * T:
+        raise ValueError("shape mismatch between hidden, packed_w and scales")
+    dev = hidden.device
+    if T > 1:
+        for t, n, dt in ((draft_ids, "draft_ids", torch.int32), (draft_probs, "draft_probs", torch.float32),
+                         (uniforms, "uniforms", torch.float32)):
+            if t is None:
+                raise ValueError(f"{n} is required when T > 1")
+            _check(t, n, dt)
+            if t.numel() != R * (T - 1):
+                raise ValueError(f"{n} must hold R*(T-1) values")
+    else:
+        draft_ids = draft_probs = uniforms = None
+    M = R * T
+    k = int(top_k)
+    lmax = torch.empty(M, dtype=torch.float32, device=dev)
+    amax = torch.empty(M, dtype=torch.int32, device=dev)
+    tids = torch.empty((M, max(k, 1)), dtype=torch.int32, device=dev)
+    tlog = torch.empty((M, max(k, 1)), dtype=torch.float32, device=dev)
+    pdr = torch.empty((R, max(T - 1, 1)), dtype=torch.float32, device=dev)
+    nacc = torch.empty(R, dtype=torch.int32, device=dev)
+    L = load_library()
+    need = L.verify_lm_head_int4_workspace_bytes(R, T, V, H)
+    if need == 0:
+        _raise(EINVAL, "verify_sampled")
+    ws = workspace if workspace is not None else _default_workspace(dev, need)
+    args = (_ptr(hidden), _ptr(packed_w), _ptr(scales), _ptr(draft_ids), _ptr(draft_probs),
+            _ptr(uniforms), R, T, V, H, k, float(temperature), _ptr(lmax), _ptr(amax), _ptr(tids),
+            _ptr(tlog), _ptr(pdr), _ptr(nacc), _ptr(ws.tensor), ws.nbytes, _stream_ptr(dev))
+    if events is None:
+        st = L.verify_lm_head_int4_sampled(*args)
+    else:
+        stream = torch.cuda.current_stream(dev)
+        st = L.verify_lm_head_int4_sampled_timed(*args, _event_handle(events[0], stream),
+                                                 _event_handle(events[1], stream))
+    if st != OK:
+        _raise(st, "verify_lm_head_int4_sampled")
+    return lmax, amax, tids, tlog, pdr[:, : max(T - 1, 0)], nacc
 
 
 def check_vocab_map(vocab_ids) -> torch.Tensor:

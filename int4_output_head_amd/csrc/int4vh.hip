@@ -103,14 +103,20 @@ constexpr int kBatchMaxRows = 4096;       // rows per launch of the batch path
 // every call; the rest is written before it is read.
 constexpr size_t kWsTicket = 0;                                   // uint32 ticket
 constexpr size_t kWsKeys = 256;                                   // uint64 [4096] batch winner keys
-constexpr size_t kWsCtlBytes = kWsKeys + (size_t)kBatchMaxRows * 8;
+constexpr size_t kWsGroupTk = kWsKeys + (size_t)kBatchMaxRows * 8;   // uint32 [64] group tickets
+constexpr size_t kWsCtlBytes = kWsGroupTk + 256;
 constexpr size_t kWsExp = kWsCtlBytes;                            // int32 [4096] step exponents
 constexpr size_t kWsPart = kWsExp + (size_t)kBatchMaxRows * 4;    // uint64 [kMaxGrid][16]
 constexpr size_t kWsFrag = kWsPart + (size_t)kMaxGrid * kMaxRows * 8;   // activation fragments
 constexpr size_t kFragBytes = (size_t)kWaves * kMaxUnitsPerWave * 2 * 3 * 64 * 16;
-constexpr size_t kWsBytes = kWsFrag + kFragBytes;
+constexpr int kMaxTopK = 16;              // largest k of the sampled epilogue
+constexpr int kSampledMaxGrid = 256;      // workgroups of a sampled call (16 groups of 16)
+constexpr size_t kWsTopK = kWsFrag + kFragBytes;                  // uint64 [256][16][kMaxTopK]
+constexpr size_t kWsGroupTopK = kWsTopK + (size_t)kSampledMaxGrid * kMaxRows * kMaxTopK * 8;
+constexpr size_t kWsBytes = kWsGroupTopK + (size_t)(kSampledMaxGrid / 16) * kMaxRows * kMaxTopK * 8;
 static_assert(kWsCtlBytes % 256 == 0 && kWsExp % 256 == 0 && kWsPart % 256 == 0 &&
-                  kWsFrag % 256 == 0, "workspace regions stay 256-byte aligned");
+                  kWsFrag % 256 == 0 && kWsTopK % 256 == 0 && kWsGroupTopK % 256 == 0,
+              "workspace regions stay 256-byte aligned");
 
 #ifndef INT4VH_WEIGHT_AUX
 #define INT4VH_WEIGHT_AUX 2                // cache policy of the weight stream: non-temporal
@@ -163,6 +169,17 @@ struct Args {
     float *logits_out;        // [M, V] or null
     const int32_t *vmap;      // [V] token id of each head row, or null (identity)
     uint64_t *part;           // [grid, M] packed (index << 32 | value bits)
+    // sampled epilogue (top-k sampling at a temperature; unused when off)
+    unsigned long long *part_topk;   // [grid, M, kTopK] per-workgroup top-k keys
+    unsigned long long *group_topk;  // [grid / 16, M, kTopK] per-group top-k keys
+    uint32_t *group_ticket;          // [64] per-group tickets, zero between calls
+    int top_k;                // k <= kTopK
+    float tau;                // temperature > 0
+    const float *dprob;       // [R, T-1] drafter probability of each draft
+    const float *unif;        // [R, T-1] uniforms in [0, 1)
+    int32_t *topk_ids;        // [M, k]
+    float *topk_logits;       // [M, k]
+    float *p_draft;           // [R, T-1]
     uint32_t *ticket;
     int32_t *exps;            // [16]
     const u32x4 *frag;        // activation fragments
@@ -188,6 +205,83 @@ __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
 __device__ __forceinline__ uint64_t pack_pair(float v, int i)
 {
     return ((uint64_t)(uint32_t)i << 32) | (uint64_t)__float_as_uint(v);
+}
+
+// Key of a (value, index) pair whose unsigned order is the argmax order:
+// larger value first, then lower index.  -0.0 is keyed as +0.0.
+__device__ __forceinline__ unsigned long long order_key(float v, int i)
+{
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u)
+        u = 0u;
+    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)i);
+}
+
+__device__ __forceinline__ float key_value(unsigned long long k)
+{
+    const uint32_t u = (uint32_t)(k >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+__device__ __forceinline__ int key_index(unsigned long long k)
+{
+    return (int)(~(uint32_t)k);
+}
+
+
+// Top-k lists hold order keys (unique: the index is part of the key),
+// sorted best first; key 0 is below every real key and marks an empty slot.
+// Insert k, dropping the last entry: straight-line code on a register array.
+template <int K>
+__device__ __forceinline__ void topk_insert(unsigned long long (&tk)[K], unsigned long long k)
+{
+#pragma unroll
+    for (int j = K - 1; j > 0; --j)
+        tk[j] = k > tk[j - 1] ? tk[j - 1] : (k > tk[j] ? k : tk[j]);
+    tk[0] = k > tk[0] ? k : tk[0];
+}
+
+// Drop the head of a sorted list.
+template <int K>
+__device__ __forceinline__ void topk_pop(unsigned long long (&tk)[K])
+{
+#pragma unroll
+    for (int j = 0; j < K - 1; ++j)
+        tk[j] = tk[j + 1];
+    tk[K - 1] = 0ull;
+}
+
+// Largest key over an aligned group of kWidth lanes (xor shuffles).
+template <int kWidth>
+__device__ __forceinline__ unsigned long long group_max(unsigned long long k)
+{
+#pragma unroll
+    for (int off = kWidth / 2; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, off);
+        const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off);
+        const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+        k = o > k ? o : k;
+    }
+    return k;
+}
+
+// kRounds rounds of "take the largest head over kWidth lanes, its owner pops
+// it": lane j of the group receives the j-th largest key of the union of the
+// lanes' sorted lists (0 past the end).
+template <int kWidth, int kRounds, int E>
+__device__ __forceinline__ unsigned long long merge_lists(unsigned long long (&tk)[E], int lane_in_group)
+{
+    unsigned long long mine = 0ull;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+        const unsigned long long h = group_max<kWidth>(tk[0]);
+        if (tk[0] == h && h != 0ull)
+            topk_pop(tk);
+        if (lane_in_group == j)
+            mine = h;
+    }
+    return mine;
 }
 
 // 16 consecutive hidden*scale products (binary32, exact) of one row.
@@ -349,10 +443,11 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
 }
 
 // ---------------------------------------------------------------- verify_kernel
-template <int kP, int kUnits, int kRing, bool kLogits>
+template <int kP, int kUnits, int kRing, bool kLogits, int kTopK>
 __global__ void __launch_bounds__(kThreads)
 verify_kernel(Args a)
 {
+    static_assert(kTopK == 0 || (kTopK <= kMaxTopK && !kLogits), "sampled epilogue");
     constexpr int kGroups = Slots<kP>::kGroups;
     constexpr int kTileBytes = kUnits * kWaves * 1024;     // LDS image of one tile (max H)
     // All LDS lives in one object: the weight ring, then the per-wave
@@ -363,6 +458,7 @@ verify_kernel(Args a)
         int fi[kWaves][kMaxRows];
         int arg[kMaxRows];
         int draft[kMaxRows];
+        int accept[kMaxRows];
         int last;
     };
     struct Lds {
@@ -379,6 +475,7 @@ verify_kernel(Args a)
     auto &s_fi = mg.fi;
     auto &s_arg = mg.arg;
     auto &s_draft = mg.draft;
+    auto &s_accept = mg.accept;
     auto &s_last = mg.last;
 
     const int lane = threadIdx.x & 63;
@@ -451,6 +548,11 @@ verify_kernel(Args a)
 
     float bv = -__builtin_huge_valf();
     int bi = 0x7FFFFFFF;
+    constexpr int kK = kTopK > 0 ? kTopK : 1;
+    unsigned long long tk[kK];               // this lane's top-k keys (sampled epilogue)
+#pragma unroll
+    for (int j = 0; j < kK; ++j)
+        tk[j] = 0ull;
     // Rows of D that hold limbs of token t are t, t + kP, t + 2*kP (those
     // with a limb index below 3).  Every lane loads (clamped to a valid
     // token) so the loads are straight-line and all in flight together.
@@ -472,6 +574,8 @@ verify_kernel(Args a)
                     bv = val;
                     bi = v;
                 }
+                if constexpr (kTopK > 0)
+                    topk_insert(tk, order_key(val, v));
                 if (kLogits)
                     a.logits_out[(size_t)rtok * V + v] = val;
             }
@@ -550,6 +654,14 @@ verify_kernel(Args a)
             bi = oi;
         }
     }
+    if constexpr (kTopK > 0) {
+        // the 16 lanes of a token merge their lists; lane n16 = j publishes
+        // the j-th key of the workgroup's top-k
+        const unsigned long long mine = merge_lists<16, kTopK>(tk, n16);
+        if (rlane && n16 < kTopK)
+            __hip_atomic_store(&a.part_topk[((size_t)b * M + rtok) * kTopK + n16], mine,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     // Publication without device-scope fences: a fence here writes back and
     // invalidates the whole L2 of the XCD, which costs tens of microseconds
     // when every workgroup does it.  The winners and the ticket are
@@ -562,14 +674,60 @@ verify_kernel(Args a)
                            __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == (uint32_t)(G - 1));
+    if constexpr (kTopK == 0) {
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(G - 1));
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
+    } else {
+        // Two levels, so that most of the merging overlaps the weight stream
+        // of the workgroups still running: the last workgroup of each group
+        // of 16 merges the group's lists into one, and the last group to
+        // finish runs the final merge.  32 threads per token; each holds a
+        // presorted chunk of kTopK/2 keys (half of one list).
+        constexpr int kE = kTopK / 2;
+        const int grp = b / 16;
+        const int gsz = min(16, G - 16 * grp);
+        const int n_grp = (G + 15) / 16;
+        if (threadIdx.x == 0) {
+            const uint32_t prev = __hip_atomic_fetch_add(&a.group_ticket[grp], 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(gsz - 1));
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
+        {
+            const int m = threadIdx.x >> 5, slot = threadIdx.x & 31;
+            const int mm = m < M ? m : M - 1;
+            const int w = (slot * kE) / kTopK, off = (slot * kE) % kTopK;
+            unsigned long long ck[kE];
+#pragma unroll
+            for (int e = 0; e < kE; ++e)
+                ck[e] = w < gsz ? __hip_atomic_load(&a.part_topk[((size_t)(16 * grp + w) * M + mm) * kTopK + off + e],
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : 0ull;
+            const unsigned long long mine = merge_lists<32, kTopK>(ck, slot);
+            if (m < M && slot < kTopK)
+                __hip_atomic_store(&a.group_topk[((size_t)grp * M + m) * kTopK + slot], mine,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __hip_atomic_store(&a.group_ticket[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            s_last = (prev == (uint32_t)(n_grp - 1));
+        }
+        __syncthreads();
+        if (!s_last)
+            return;
     }
-    __syncthreads();
-    if (!s_last)
-        return;
 
     // ---------------- last workgroup: merge, write, accept, reset
     // One memory round trip: every load below is issued before any is used.
@@ -650,13 +808,72 @@ verify_kernel(Args a)
         s_arg[m] = id;
     }
     __syncthreads();
-    if (threadIdx.x < (unsigned)a.R) {
-        const int req = threadIdx.x;
+    if constexpr (kTopK == 0) {
+        if (threadIdx.x < (unsigned)a.R) {
+            const int req = threadIdx.x;
+            const int T = a.T;
+            int n = 0;
+            while (n < T - 1 && s_arg[req * T + n] == s_draft[req * (T - 1) + n])
+                ++n;
+            a.n_acc[req] = n;
+        }
+    } else {
+        // Sampled epilogue, final merge over the group lists (32 threads
+        // per token, a presorted half list each), then the token's target
+        // probability of its draft from the k logits (top-k sampling at
+        // temperature tau), in the same order on every call.
+        constexpr int kE = kTopK / 2;
+        const int m = threadIdx.x >> 5;
+        const int slot = threadIdx.x & 31;
+        const int mm = m < M ? m : M - 1;
+        const int n_grp = (G + 15) / 16;
+        const int w = (slot * kE) / kTopK, off = (slot * kE) % kTopK;
+        unsigned long long ck[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            ck[e] = w < n_grp ? __hip_atomic_load(&a.group_topk[((size_t)w * M + mm) * kTopK + off + e],
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : 0ull;
         const int T = a.T;
-        int n = 0;
-        while (n < T - 1 && s_arg[req * T + n] == s_draft[req * (T - 1) + n])
-            ++n;
-        a.n_acc[req] = n;
+        const int req = mm / T, t = mm % T;
+        const bool drafted = t < T - 1;
+        const int d = drafted ? s_draft[req * (T - 1) + t] : -1;
+        float lmax = 0.0f, sum = 0.0f, e_d = 0.0f;
+        for (int j = 0; j < a.top_k; ++j) {
+            const unsigned long long h = group_max<32>(ck[0]);
+            if (ck[0] == h)
+                topk_pop(ck);
+            const float hv = key_value(h);
+            const int hi = key_index(h);
+            if (j == 0)
+                lmax = hv;
+            const float e = expf((hv - lmax) / a.tau);
+            sum += e;
+            if (hi == d)
+                e_d = e;
+            if (slot == j && m < M) {
+                a.topk_ids[m * a.top_k + j] = hi;
+                a.topk_logits[m * a.top_k + j] = hv;
+            }
+        }
+        if (slot == 0 && m < M) {
+            int ok = 0;
+            if (drafted) {
+                const int di = req * (T - 1) + t;
+                const float p = e_d / sum;
+                a.p_draft[di] = p;
+                ok = a.unif[di] * a.dprob[di] < p;
+            }
+            s_accept[m] = ok;
+        }
+        __syncthreads();
+        if (threadIdx.x < (unsigned)a.R) {
+            const int r = threadIdx.x;
+            int n = 0;
+            while (n < T - 1 && s_accept[r * T + n])
+                ++n;
+            a.n_acc[r] = n;
+        }
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -746,28 +963,6 @@ struct RArgs {
 __device__ __forceinline__ size_t rfrag_index(int tb, int n_steps, int s, int h, int l, int lane)
 {
     return ((((size_t)tb * n_steps + s) * 2 + h) * 3 + l) * 64 + lane;
-}
-
-// Key of a (value, index) pair whose unsigned order is the argmax order:
-// larger value first, then lower index.  -0.0 is keyed as +0.0.
-__device__ __forceinline__ unsigned long long order_key(float v, int i)
-{
-    uint32_t u = __float_as_uint(v);
-    if (u == 0x80000000u)
-        u = 0u;
-    u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return ((unsigned long long)u << 32) | (unsigned long long)(~(uint32_t)i);
-}
-
-__device__ __forceinline__ float key_value(unsigned long long k)
-{
-    const uint32_t u = (uint32_t)(k >> 32);
-    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
-}
-
-__device__ __forceinline__ int key_index(unsigned long long k)
-{
-    return (int)(~(uint32_t)k);
 }
 
 // ---------------------------------------------------------------- stage_rows_kernel
@@ -1182,41 +1377,52 @@ struct Pair {
 };
 
 // Ring depth: three tiles in flight while they fit in LDS, else two.
-template <int kP, int kUnits, bool kLogits>
+template <int kP, int kUnits, bool kLogits, int kTopK>
 Pair make_pair()
 {
     constexpr int kRing = kUnits <= 5 ? 3 : 2;
-    return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits>};
+    return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits, kTopK>};
 }
 
-template <int kP, bool kLogits>
+template <int kP, bool kLogits, int kTopK>
 Pair pick(int units)
 {
     switch (units) {
-    case 1: return make_pair<kP, 1, kLogits>();
-    case 2: return make_pair<kP, 2, kLogits>();
-    case 3: return make_pair<kP, 3, kLogits>();
-    case 4: return make_pair<kP, 4, kLogits>();
-    case 5: return make_pair<kP, 5, kLogits>();
-    case 6: return make_pair<kP, 6, kLogits>();
-    case 7: return make_pair<kP, 7, kLogits>();
-    default: return make_pair<kP, 8, kLogits>();
+    case 1: return make_pair<kP, 1, kLogits, kTopK>();
+    case 2: return make_pair<kP, 2, kLogits, kTopK>();
+    case 3: return make_pair<kP, 3, kLogits, kTopK>();
+    case 4: return make_pair<kP, 4, kLogits, kTopK>();
+    case 5: return make_pair<kP, 5, kLogits, kTopK>();
+    case 6: return make_pair<kP, 6, kLogits, kTopK>();
+    case 7: return make_pair<kP, 7, kLogits, kTopK>();
+    default: return make_pair<kP, 8, kLogits, kTopK>();
     }
 }
 
-template <bool kLogits>
+template <bool kLogits, int kTopK>
 Pair pick_rows(int M, int units, int *kp)
 {
     if (M <= 5) {
         *kp = 5;
-        return pick<5, kLogits>(units);
+        return pick<5, kLogits, kTopK>(units);
     }
     if (M <= 8) {
         *kp = 8;
-        return pick<8, kLogits>(units);
+        return pick<8, kLogits, kTopK>(units);
     }
     *kp = 16;
-    return pick<16, kLogits>(units);
+    return pick<16, kLogits, kTopK>(units);
+}
+
+// Kernel pair for a call: greedy (with or without every logit written) or
+// the sampled epilogue with an 8- or 16-entry top-k list.
+Pair pick_kernels(int M, int units, bool logits, int top_k, int *kp)
+{
+    if (top_k > 8)
+        return pick_rows<false, 16>(M, units, kp);
+    if (top_k > 0)
+        return pick_rows<false, 8>(M, units, kp);
+    return logits ? pick_rows<true, 0>(M, units, kp) : pick_rows<false, 0>(M, units, kp);
 }
 
 // K steps of the batch path (128 channels each, rounded up to even).
@@ -1327,10 +1533,21 @@ int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const 
     return record_event(ev1, s, "event record after verify_rows kernel");
 }
 
+// Outputs and parameters of the sampled epilogue.
+struct Sampled {
+    int top_k;
+    float tau;
+    const float *dprob;
+    const float *unif;
+    int32_t *topk_ids;
+    float *topk_logits;
+    float *p_draft;
+};
+
 int launch_verify(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
                   int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
                   float *lout, void *ws, size_t ws_bytes, void *stream, void *ev0 = nullptr,
-                  void *ev1 = nullptr, const int32_t *vmap = nullptr)
+                  void *ev1 = nullptr, const int32_t *vmap = nullptr, const Sampled *smp = nullptr)
 {
     const int st = validate(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, ws,
                             ws_bytes);
@@ -1338,6 +1555,8 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
         return st;
     if (vmap && !aligned(vmap, 4))
         return INT4VH_EALIGN;
+    if (smp && R * T > kMaxRows)
+        return INT4VH_EUNSUPPORTED;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
@@ -1350,6 +1569,16 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
                            wsb, dev, s, ev0, ev1);
     Args a;
     a.vmap = vmap;
+    a.part_topk = reinterpret_cast<unsigned long long *>(wsb + kWsTopK);
+    a.group_topk = reinterpret_cast<unsigned long long *>(wsb + kWsGroupTopK);
+    a.group_ticket = reinterpret_cast<uint32_t *>(wsb + kWsGroupTk);
+    a.top_k = smp ? smp->top_k : 0;
+    a.tau = smp ? smp->tau : 1.0f;
+    a.dprob = smp ? smp->dprob : nullptr;
+    a.unif = smp ? smp->unif : nullptr;
+    a.topk_ids = smp ? smp->topk_ids : nullptr;
+    a.topk_logits = smp ? smp->topk_logits : nullptr;
+    a.p_draft = smp ? smp->p_draft : nullptr;
     a.hidden = static_cast<const uint16_t *>(hidden);
     a.w = w;
     a.scales = static_cast<const uint16_t *>(scales);
@@ -1377,8 +1606,10 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
         grid = kMaxGrid;
     if (grid > a.n_tiles)
         grid = a.n_tiles;
+    if (smp && grid > kSampledMaxGrid)
+        grid = kSampledMaxGrid;
     int kp = 16;
-    const Pair fn = lout ? pick_rows<true>(a.M, units, &kp) : pick_rows<false>(a.M, units, &kp);
+    const Pair fn = pick_kernels(a.M, units, lout != nullptr, smp ? smp->top_k : 0, &kp);
     hipLaunchKernelGGL(fn.stage, dim3(kp), dim3(kStageThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess)
@@ -1461,6 +1692,47 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
     return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
                          n_accepted, logits_out, workspace, workspace_bytes, stream, nullptr,
                          nullptr, vocab_ids);
+}
+
+int verify_lm_head_int4_sampled_timed(const void *hidden, const uint8_t *packed_w,
+                                      const void *scales, const int32_t *draft_ids,
+                                      const float *draft_probs, const float *uniforms, int R, int T,
+                                      int V, int H, int top_k, float temperature,
+                                      float *logits_max, int32_t *argmax_ids, int32_t *topk_ids,
+                                      float *topk_logits, float *p_draft, int32_t *n_accepted,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      void *event_before, void *event_after)
+{
+    if (top_k < 1 || top_k > kMaxTopK || top_k > V || !(temperature > 0.0f) ||
+        !(temperature < __builtin_huge_valf()))
+        return INT4VH_EINVAL;
+    if (!topk_ids || !topk_logits)
+        return INT4VH_EINVAL;
+    if (T > 1 && (!draft_probs || !uniforms || !p_draft))
+        return INT4VH_EINVAL;
+    if (!aligned(topk_ids, 4) || !aligned(topk_logits, 4) || (draft_probs && !aligned(draft_probs, 4)) ||
+        (uniforms && !aligned(uniforms, 4)) || (p_draft && !aligned(p_draft, 4)))
+        return INT4VH_EALIGN;
+    // (more than 16 rows: INT4VH_EUNSUPPORTED from launch_verify, after the
+    // common validation)
+    const Sampled smp{top_k, temperature, draft_probs, uniforms, topk_ids, topk_logits, p_draft};
+    return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
+                         n_accepted, nullptr, workspace, workspace_bytes, stream, event_before,
+                         event_after, nullptr, &smp);
+}
+
+int verify_lm_head_int4_sampled(const void *hidden, const uint8_t *packed_w, const void *scales,
+                                const int32_t *draft_ids, const float *draft_probs,
+                                const float *uniforms, int R, int T, int V, int H, int top_k,
+                                float temperature, float *logits_max, int32_t *argmax_ids,
+                                int32_t *topk_ids, float *topk_logits, float *p_draft,
+                                int32_t *n_accepted, void *workspace, size_t workspace_bytes,
+                                void *stream)
+{
+    return verify_lm_head_int4_sampled_timed(hidden, packed_w, scales, draft_ids, draft_probs,
+                                             uniforms, R, T, V, H, top_k, temperature, logits_max,
+                                             argmax_ids, topk_ids, topk_logits, p_draft, n_accepted,
+                                             workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 int verify_lm_head_int4_check_vocab_map(const int32_t *vocab_ids, int V, int32_t *n_bad_out,

@@ -48,7 +48,10 @@ def test_header_declares_expected_api():
     for n in ("verify_lm_head_int4", "verify_lm_head_int4_batch", "verify_lm_head_int4_batch_timed",
               "verify_lm_head_int4_workspace_bytes", "verify_lm_head_int4_workspace_init",
               "verify_lm_head_int4_check_weights", "verify_lm_head_int4_status_string",
-              "verify_lm_head_int4_last_error", "requant_lm_head_int4_amax",
+              "verify_lm_head_int4_last_error", "verify_lm_head_int4_mapped",
+              "verify_lm_head_int4_check_vocab_map", "verify_lm_head_int4_sampled",
+              "verify_lm_head_int4_sampled_timed",
+              "requant_lm_head_int4_amax",
               "requant_lm_head_int4_scales", "requant_lm_head_int4_pack",
               "requant_lm_head_int4_pack_timed", "requant_lm_head_int4"):
         assert n in names, n
@@ -188,3 +191,31 @@ def test_requant_rejects_invalid_arguments(lib):
     assert rq(a, 0, 10, 64, a, 5, 4, a, a, a, None) == EINVAL
     assert rq(a, 0, 10, 64, a, 0, 4, a, P(A + 2), a, None) == EALIGN
     assert rq(a, 0, 1 << 28, 8192, a, 0, 4, a, a, a, None) == EUNSUPPORTED
+
+
+def test_sampled_rejects_invalid_arguments(lib):
+    P, i32 = ctypes.c_void_p, ctypes.c_int
+    f = lib.verify_lm_head_int4_sampled
+    f.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, P, P, P, P, P, P, P,
+                  ctypes.c_size_t, P]
+    a = P(A)
+
+    def scall(R=1, T=4, V=100, H=256, k=8, tau=1.0, dprob=A, unif=A, pdr=A, tids=A, tlog=A, ws_bytes=WS):
+        return f(a, a, a, a, P(dprob), P(unif), R, T, V, H, k, tau, a, a, P(tids), P(tlog), P(pdr), a,
+                 a, ws_bytes, None)
+
+    assert scall(k=0) == EINVAL
+    assert scall(k=17) == EINVAL
+    assert scall(k=8, V=7) == EINVAL                  # k > V
+    assert scall(tau=0.0) == EINVAL
+    assert scall(tau=-1.0) == EINVAL
+    assert scall(tau=float("nan")) == EINVAL
+    assert scall(tau=float("inf")) == EINVAL
+    assert scall(dprob=0) == EINVAL
+    assert scall(unif=0) == EINVAL
+    assert scall(pdr=0) == EINVAL
+    assert scall(tids=0) == EINVAL
+    assert scall(tlog=A + 2) == EALIGN
+    assert scall(R=2, T=9) == EUNSUPPORTED            # more than 16 rows
+    assert scall(R=1, T=17) == EINVAL
+    assert scall(ws_bytes=100) == EWORKSPACE

@@ -1,0 +1,236 @@
+"""GPU parity of sampled verification (verify_lm_head_int4_sampled: top-k
+sampling at a temperature, fused into the weight stream) against the oracle
+(oracle/sampled.py).  Needs an MI355X and the built library.
+
+Parity rule (from the logit tolerance tol[r] = 2e-3 * max_v |oracle logit|):
+  * top-k: the GPU's k ids are distinct, its j-th logit is within tol of the
+    oracle's j-th, and the oracle logit at its j-th id is within tol of the
+    oracle's j-th (several id lists are correct when logits nearly tie);
+  * p_draft: a probability of top-k sampling at temperature tau moves by at
+    most a factor exp(2 tol / tau) when every logit moves by at most tol, so
+    |p_gpu - p_oracle| <= p_oracle * (exp(2 tol / tau) - 1) + 1e-6 when both
+    top-k sets contain the draft, and the draft's logit is within tol of the
+    k-th logit whenever only one of them does;
+  * n_accepted: exactly the count recomputed from the GPU's own p_draft,
+    uniforms and draft probabilities (binary32 product and compare), and the
+    oracle's unless the first differing decision is a near tie
+    (|u q - p_oracle| within the p_draft bound).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from int4_output_head_amd import synth  # noqa: E402
+from oracle import sampled as sm  # noqa: E402
+
+from . import parity  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(f"[gpu-sampled] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def vh():
+    from int4_output_head_amd import binding
+    binding.load_library()
+    assert torch.cuda.is_available(), "no GPU visible"
+    return binding
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def make_drafts(lg, R, T, k, seed):
+    """Drafts that hit the argmax, other top-k entries, and tokens outside."""
+    rng = np.random.default_rng(seed)
+    ids, _ = sm.topk_rows(lg, min(k, lg.shape[1]))
+    d = np.zeros((R, max(T - 1, 0)), np.int32)
+    for i in range(R):
+        for t in range(T - 1):
+            r = i * T + t
+            c = rng.random()
+            if c < 0.6:
+                d[i, t] = ids[r, 0]
+            elif c < 0.85:
+                d[i, t] = ids[r, rng.integers(0, ids.shape[1])]
+            else:
+                d[i, t] = rng.integers(0, lg.shape[1])
+    q = rng.uniform(0.3, 1.0, size=d.shape).astype(np.float32)
+    q[rng.random(d.shape) < 0.3] = 1.0                      # copied-from-context drafts
+    u = rng.random(d.shape).astype(np.float32)
+    return d, q, u
+
+
+def run(vh, inp, d, q, u, R, T, V, H, k, tau):
+    T1 = T - 1
+    out = vh.verify_sampled(dev(inp["hidden"], torch.float16).reshape(R, T, H), dev(inp["packed"]),
+                            dev(inp["scales"], torch.float16),
+                            dev(d) if T1 else None, dev(q) if T1 else None, dev(u) if T1 else None,
+                            top_k=k, temperature=tau)
+    torch.cuda.synchronize()
+    names = ("logits_max", "argmax_ids", "topk_ids", "topk_logits", "p_draft", "n_accepted")
+    return {n: t.cpu().numpy() for n, t in zip(names, out)}
+
+
+def check(g, o, lg, d, q, u, R, T, k, tau):
+    M = R * T
+    amax = np.abs(lg.astype(np.float64)).max(axis=1)
+    tol = 2e-3 * amax
+    stats = dict(topk_ids_differ=0, p_max_rel_err=0.0, accept_near=0)
+    # greedy outputs: the usual rule
+    gg = dict(logits_max=g["logits_max"], argmax_ids=g["argmax_ids"], n_accepted=np.zeros(R, np.int64))
+    oo = dict(o)
+    oo["n_accepted"] = np.zeros(R, np.int64)
+    parity.check(gg, oo, R, T, np.full((R, max(T - 1, 0)), -1, np.int32))
+    assert np.array_equal(g["topk_ids"][:, 0], g["argmax_ids"])
+    assert np.array_equal(g["topk_logits"][:, 0], g["logits_max"])
+    for r in range(M):
+        gi, gv = g["topk_ids"][r], g["topk_logits"][r].astype(np.float64)
+        oi, ov = o["topk_ids"][r], o["topk_logits"][r].astype(np.float64)
+        assert len(set(gi.tolist())) == k and np.all((gi >= 0) & (gi < lg.shape[1]))
+        assert np.all(np.abs(gv - ov) <= tol[r] + 0.0), (r, gv, ov)
+        assert np.all(np.abs(lg[r, gi].astype(np.float64) - ov) <= tol[r]), r
+        assert np.all(gv[:-1] >= gv[1:])
+        if not np.array_equal(gi, oi):
+            stats["topk_ids_differ"] += 1
+    if T == 1:
+        assert np.array_equal(g["n_accepted"], np.zeros(R))
+        return stats
+    # acceptance from the GPU's own probabilities (binary32 product and compare)
+    own = np.zeros(R, np.int64)
+    for i in range(R):
+        n = 0
+        while n < T - 1 and np.float32(u[i, n]) * np.float32(q[i, n]) < g["p_draft"][i, n]:
+            n += 1
+        own[i] = n
+    assert np.array_equal(g["n_accepted"], own)
+    near = np.zeros((R, T - 1), bool)
+    for i in range(R):
+        for t in range(T - 1):
+            r = i * T + t
+            pg, po = float(g["p_draft"][i, t]), float(o["p_draft"][i, t])
+            bound = po * (math.exp(2 * tol[r] / tau) - 1) + 1e-6
+            in_g = d[i, t] in g["topk_ids"][r]
+            in_o = d[i, t] in o["topk_ids"][r]
+            if in_g and in_o:
+                assert abs(pg - po) <= bound, (i, t, pg, po, bound)
+                if po > 0:
+                    stats["p_max_rel_err"] = max(stats["p_max_rel_err"], abs(pg - po) / po)
+            elif in_g != in_o:
+                # the draft sits at the edge of the top-k: within tol of the k-th logit
+                assert abs(float(lg[r, d[i, t]]) - float(o["topk_logits"][r, -1])) <= tol[r], (i, t)
+                bound = 1.0
+            else:
+                assert pg == 0.0 and po == 0.0
+            near[i, t] = abs(float(u[i, t]) * float(q[i, t]) - po) <= bound
+    for i in range(R):
+        if g["n_accepted"][i] != o["n_accepted"][i]:
+            first = min(g["n_accepted"][i], o["n_accepted"][i])
+            assert near[i, first], f"request {i}: n_accepted {g['n_accepted'][i]} vs {o['n_accepted'][i]}"
+            stats["accept_near"] += 1
+    return stats
+
+
+@pytest.mark.parametrize("R,T,V,H,k,tau", [(1, 4, 300, 64, 8, 1.0), (1, 16, 5000, 512, 16, 0.7),
+                                           (2, 8, 4097, 256, 5, 1.3), (4, 4, 999, 96, 16, 1.0),
+                                           (1, 1, 8192, 5120, 8, 1.0), (3, 5, 2000, 160, 1, 1.0),
+                                           (16, 1, 700, 128, 12, 2.0)])
+def test_sampled_parity(vh, oracle_mod, R, T, V, H, k, tau):
+    say(f"sampled R={R} T={T} V={V} H={H} k={k} tau={tau}")
+    inp = synth.uniform_inputs(R * T, V, H, seed=R * 31 + T + V + H + k)
+    lg = oracle_mod.logits(inp["hidden"], inp["packed"], inp["scales"], R * T, V, H)
+    d, q, u = make_drafts(lg, R, T, k, seed=V)
+    o = sm.verify_sampled(inp["hidden"], inp["packed"], inp["scales"], d, q, u, R, T, V, H, k, tau)
+    g = run(vh, inp, d, q, u, R, T, V, H, k, tau)
+    st = check(g, o, lg, d, q, u, R, T, k, tau)
+    say(f"stats {st}")
+
+
+def test_sampled_full_vocab_t16(vh, oracle_mod):
+    """The headline shape: V=151936, H=5120, T=16, top-16 at tau = 1."""
+    cfg = synth.CONFIGS["full_t16"]
+    head = synth.make_head(cfg)
+    x = synth.make_hidden(cfg, 0)
+    lg = oracle_mod.logits(x, head["packed"], head["scales"], cfg.M, cfg.V, cfg.H, n_threads=16)
+    inp = dict(hidden=x, packed=head["packed"], scales=head["scales"])
+    d, q, u = make_drafts(lg, 1, 16, 16, seed=1)
+    ids, vals = sm.topk_rows(lg, 16)
+    idx, mx, gap, amax = oracle_mod.argmax_rows(lg)
+    p, n = sm.sampled_accept(ids, vals, d, q, u, 1, 16, 1.0)
+    o = dict(logits=lg, logits_max=mx, argmax_ids=idx, gap=gap, amax=amax, topk_ids=ids,
+             topk_logits=vals, p_draft=p, n_accepted=n)
+    g = run(vh, inp, d, q, u, 1, 16, cfg.V, cfg.H, 16, 1.0)
+    st = check(g, o, lg, d, q, u, 1, 16, 16, 1.0)
+    say(f"full-vocab T=16 stats {st}")
+
+
+def test_sampled_int_exact_bitexact(vh, oracle_mod):
+    """Integer-exact inputs: the top-k ids (ties broken by the lowest row
+    across tiles and workgroups) and logits equal the oracle's bit for bit."""
+    R, T, V, H, k = 2, 8, 3000, 512, 16
+    inp = synth.int_exact_inputs(R * T, V, H, seed=12)
+    lg = oracle_mod.logits(inp["hidden"], inp["packed"], inp["scales"], R * T, V, H)
+    d, q, u = make_drafts(lg, R, T, k, seed=2)
+    o = sm.verify_sampled(inp["hidden"], inp["packed"], inp["scales"], d, q, u, R, T, V, H, k, 1.0)
+    g = run(vh, inp, d, q, u, R, T, V, H, k, 1.0)
+    assert np.array_equal(g["topk_ids"], o["topk_ids"])
+    assert np.array_equal(g["topk_logits"], o["topk_logits"])
+    assert np.allclose(g["p_draft"], o["p_draft"], rtol=1e-5, atol=1e-7)
+    check(g, o, lg, d, q, u, R, T, k, 1.0)
+
+
+def test_k1_is_greedy_acceptance(vh):
+    """top_k = 1: the argmax has probability 1, every other token 0, so with
+    draft probabilities 1 and uniforms below 1 the sampled count equals the
+    greedy count of verify_lm_head_int4."""
+    R, T, V, H = 1, 16, 20000, 1024
+    inp = synth.uniform_inputs(T, V, H, seed=77)
+    x = dev(inp["hidden"], torch.float16)
+    w = dev(inp["packed"])
+    s = dev(inp["scales"], torch.float16)
+    _, ids, _ = vh.verify(x, w, s, dev(np.zeros(T - 1, np.int32)))
+    d = ids[: T - 1].clone()
+    d[9] = (d[9] + 1) % V
+    q = torch.ones(T - 1, dtype=torch.float32, device="cuda")
+    u = torch.full((T - 1,), 0.999, dtype=torch.float32, device="cuda")
+    lmax_g, ids_g, n_g = vh.verify(x, w, s, d)
+    out = vh.verify_sampled(x.reshape(1, T, H), w, s, d, q, u, top_k=1, temperature=1.0)
+    torch.cuda.synchronize()
+    assert int(out[5].item()) == int(n_g.item()) == 9
+    assert torch.equal(out[0], lmax_g) and torch.equal(out[1], ids_g)
+    assert torch.all(out[4][0, :9] == 1.0) and float(out[4][0, 9]) == 0.0
+
+
+def test_sampled_then_greedy_workspace_reuse(vh):
+    """Sampled and greedy calls alternate on one workspace; each call leaves
+    it ready for the next (results equal fresh calls)."""
+    R, T, V, H = 1, 8, 6000, 256
+    inp = synth.uniform_inputs(T, V, H, seed=5)
+    x = dev(inp["hidden"], torch.float16)
+    w = dev(inp["packed"])
+    s = dev(inp["scales"], torch.float16)
+    d = dev(np.arange(T - 1, dtype=np.int32))
+    q = torch.ones(T - 1, dtype=torch.float32, device="cuda")
+    u = torch.rand(T - 1, dtype=torch.float32, device="cuda")
+    ws = vh.Workspace(vh.workspace_bytes(1, T, V, H), x.device)
+    a1 = vh.verify_sampled(x.reshape(1, T, H), w, s, d, q, u, top_k=16, workspace=ws)
+    b1 = vh.verify(x, w, s, d, workspace=ws)
+    a2 = vh.verify_sampled(x.reshape(1, T, H), w, s, d, q, u, top_k=16, workspace=ws)
+    b2 = vh.verify(x, w, s, d, workspace=ws)
+    torch.cuda.synchronize()
+    for p1, p2 in zip(a1, a2):
+        assert torch.equal(p1, p2)
+    for p1, p2 in zip(b1, b2):
+        assert torch.equal(p1, p2)
