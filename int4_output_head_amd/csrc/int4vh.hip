@@ -230,58 +230,139 @@ __device__ __forceinline__ int key_index(unsigned long long k)
 }
 
 
-// Top-k lists hold order keys (unique: the index is part of the key),
-// sorted best first; key 0 is below every real key and marks an empty slot.
-// Insert k, dropping the last entry: straight-line code on a register array.
-template <int K>
-__device__ __forceinline__ void topk_insert(unsigned long long (&tk)[K], unsigned long long k)
+// Top-k lists of the sampled epilogue are distributed over an aligned group
+// of 16 lanes (one DPP row): lane j of the group holds the rank-j order key
+// (best first; keys are unique because the index is part of the key, and key
+// 0, below every real key, marks an empty rank).
+
+__device__ __forceinline__ unsigned long long key_readlane(unsigned long long k, int src)
 {
-#pragma unroll
-    for (int j = K - 1; j > 0; --j)
-        tk[j] = k > tk[j - 1] ? tk[j - 1] : (k > tk[j] ? k : tk[j]);
-    tk[0] = k > tk[0] ? k : tk[0];
+    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, src);
+    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), src);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
-// Drop the head of a sorted list.
-template <int K>
-__device__ __forceinline__ void topk_pop(unsigned long long (&tk)[K])
+__device__ __forceinline__ unsigned long long key_shfl(unsigned long long k, int src)
 {
-#pragma unroll
-    for (int j = 0; j < K - 1; ++j)
-        tk[j] = tk[j + 1];
-    tk[K - 1] = 0ull;
+    const uint32_t lo = __shfl((uint32_t)k, src);
+    const uint32_t hi = __shfl((uint32_t)(k >> 32), src);
+    return ((unsigned long long)hi << 32) | lo;
 }
 
-// Largest key over an aligned group of kWidth lanes (xor shuffles).
-template <int kWidth>
-__device__ __forceinline__ unsigned long long group_max(unsigned long long k)
+// The key of the previous lane of the DPP row (row_shr:1; lane 0 of the row
+// gets 0).
+__device__ __forceinline__ unsigned long long key_row_prev(unsigned long long k)
 {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, 0x111, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), 0x111, 0xF, 0xF, false);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// Insert `key` (equal on the group's lanes) into the distributed list whose
+// rank-j entry this lane holds; the last entry drops out.
+__device__ __forceinline__ unsigned long long dlist_insert(unsigned long long mine, unsigned long long key)
+{
+    const bool first = (threadIdx.x & 15) == 0;          // rank 0 of the group
+    const unsigned long long up = key_row_prev(mine);    // rank j-1 (an empty rank is 0)
+    return (!first && key > up) ? up : (key > mine ? key : mine);
+}
+
+// 64-bit DPP move within a row of 16 lanes (lanes whose source is outside
+// the row get 0).
+template <int kCtrl>
+__device__ __forceinline__ unsigned long long key_dpp(unsigned long long k)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, kCtrl, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), kCtrl, 0xF, 0xF, false);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// The key of lane j ^ S of the row: quad_perm for S = 1, 2; row_shl:4 /
+// row_shr:4 for S = 4; row_ror:8 for S = 8.
+template <int S>
+__device__ __forceinline__ unsigned long long key_row_xor(unsigned long long k, int j)
+{
+    if constexpr (S == 1)
+        return key_dpp<0xB1>(k);
+    else if constexpr (S == 2)
+        return key_dpp<0x4E>(k);
+    else if constexpr (S == 4) {
+        // both moves with every lane active (a DPP move inside a divergent
+        // branch reads inactive source lanes as 0), then the select
+        const unsigned long long from_above = key_dpp<0x104>(k);
+        const unsigned long long from_below = key_dpp<0x114>(k);
+        return (j & 4) ? from_below : from_above;
+    } else
+        return key_dpp<0x128>(k);
+}
+
+// Compare-exchange with lane j ^ S: keep the larger key or the smaller one.
+template <int S>
+__device__ __forceinline__ unsigned long long key_cex(unsigned long long c, int j, bool keep_max)
+{
+    const unsigned long long o = key_row_xor<S>(c, j);
+    return (keep_max == (c > o)) ? c : o;
+}
+
+// Sort the 16 keys of a row best first (bitonic network, 10 stages).
+__device__ __forceinline__ unsigned long long row_sort16(unsigned long long c, int j)
+{
+    c = key_cex<1>(c, j, ((j & 1) == 0) == ((j & 2) == 0));
+    c = key_cex<2>(c, j, ((j & 2) == 0) == ((j & 4) == 0));
+    c = key_cex<1>(c, j, ((j & 1) == 0) == ((j & 4) == 0));
+    c = key_cex<4>(c, j, ((j & 4) == 0) == ((j & 8) == 0));
+    c = key_cex<2>(c, j, ((j & 2) == 0) == ((j & 8) == 0));
+    c = key_cex<1>(c, j, ((j & 1) == 0) == ((j & 8) == 0));
+    c = key_cex<8>(c, j, (j & 8) == 0);
+    c = key_cex<4>(c, j, (j & 4) == 0);
+    c = key_cex<2>(c, j, (j & 2) == 0);
+    return key_cex<1>(c, j, (j & 1) == 0);
+}
+
+// Top 16 of two distributed lists: a = rank-j key of list A, b_rev = rank
+// (15-j) key of list B.  max(A[j], B[15-j]) is a bitonic sequence holding the
+// 16 largest keys; four compare-exchange stages sort it (the lower lane of
+// each pair keeps the larger key).
+__device__ __forceinline__ unsigned long long dlist_merge(unsigned long long a, unsigned long long b_rev,
+                                                          int lane)
+{
+    const int j = lane & 15;
+    const unsigned long long c = a > b_rev ? a : b_rev;
+    return key_cex<1>(key_cex<2>(key_cex<4>(key_cex<8>(c, j, (j & 8) == 0), j, (j & 4) == 0), j,
+                                 (j & 2) == 0),
+                      j, (j & 1) == 0);
+}
+
+// Merge up to 16 published top-k lists ([n_lists][M][kTopK] keys, rank
+// order) per token; a workgroup of 512 threads, wave w handling tokens 2w
+// and 2w+1 with 32 lanes each.  Each half of the 32 lanes folds the lists of
+// its parity (all loads issued first), then the halves merge; every lane
+// returns the rank-(lane & 15) key of its token's merged list.
+template <int kTopK>
+__device__ __forceinline__ unsigned long long merge_topk_lists(const unsigned long long *lists, int n_lists,
+                                                               int M, int lane)
+{
+    const int wave = threadIdx.x >> 6;
+    const int m = 2 * wave + (lane >> 5);
+    const int mm = m < M ? m : M - 1;
+    const int h = (lane >> 4) & 1;
+    const int j = lane & 15;
+    unsigned long long e[8];
 #pragma unroll
-    for (int off = kWidth / 2; off >= 1; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)k, off);
-        const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off);
-        const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-        k = o > k ? o : k;
+    for (int i = 0; i < 8; ++i) {
+        const int w = 2 * i + h;
+        const int r = i == 0 ? j : 15 - j;       // the first list by rank, the others reversed
+        e[i] = (w < n_lists && r < kTopK)
+                   ? __hip_atomic_load(&lists[((size_t)w * M + mm) * kTopK + r], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0ull;
     }
-    return k;
-}
-
-// kRounds rounds of "take the largest head over kWidth lanes, its owner pops
-// it": lane j of the group receives the j-th largest key of the union of the
-// lanes' sorted lists (0 past the end).
-template <int kWidth, int kRounds, int E>
-__device__ __forceinline__ unsigned long long merge_lists(unsigned long long (&tk)[E], int lane_in_group)
-{
-    unsigned long long mine = 0ull;
+    unsigned long long c = e[0];
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-        const unsigned long long h = group_max<kWidth>(tk[0]);
-        if (tk[0] == h && h != 0ull)
-            topk_pop(tk);
-        if (lane_in_group == j)
-            mine = h;
-    }
-    return mine;
+    for (int i = 1; i < 8; ++i)
+        if (2 * i < n_lists)
+            c = dlist_merge(c, e[i], lane);
+    return dlist_merge(c, key_shfl(c, ((lane ^ 16) & ~15) | (15 - j)), lane);
 }
 
 // 16 consecutive hidden*scale products (binary32, exact) of one row.
@@ -548,11 +629,9 @@ verify_kernel(Args a)
 
     float bv = -__builtin_huge_valf();
     int bi = 0x7FFFFFFF;
-    constexpr int kK = kTopK > 0 ? kTopK : 1;
-    unsigned long long tk[kK];               // this lane's top-k keys (sampled epilogue)
-#pragma unroll
-    for (int j = 0; j < kK; ++j)
-        tk[j] = 0ull;
+    // sampled epilogue: the token's distributed top-k list (lanes 0-15: token
+    // 2*wave, lanes 16-31: token 2*wave+1; rank = n16)
+    unsigned long long dl = 0ull;
     // Rows of D that hold limbs of token t are t, t + kP, t + 2*kP (those
     // with a limb index below 3).  Every lane loads (clamped to a valid
     // token) so the loads are straight-line and all in flight together.
@@ -566,6 +645,7 @@ verify_kernel(Args a)
 #pragma unroll
             for (int w = 0; w < kWaves; ++w)
                 code += (long long)s_part[buf][w][rt + kP * j][n16];
+        unsigned long long key = 0ull;
         if (rlane) {
             const int v = (b + k * G) * kTileRows + n16;
             const float val = (float)ldexp((double)code, rexp);   // the one rounding
@@ -575,9 +655,36 @@ verify_kernel(Args a)
                     bi = v;
                 }
                 if constexpr (kTopK > 0)
-                    topk_insert(tk, order_key(val, v));
+                    key = order_key(val, v);
                 if (kLogits)
                     a.logits_out[(size_t)rtok * V + v] = val;
+            }
+        }
+        if constexpr (kTopK > 0) {
+            // insert the tile's keys that beat the list's last kept rank: a
+            // sort and one merge when a group has more than two, else one per
+            // group and iteration (wave-uniform control flow, all lanes active)
+            const unsigned long long th0 = key_readlane(dl, kTopK - 1);
+            const unsigned long long th1 = key_readlane(dl, 16 + kTopK - 1);
+            const bool is_cand = key > (lane < 16 ? th0 : th1);
+            unsigned long long cand = __ballot(is_cand);
+            if (__builtin_popcount((uint32_t)cand & 0xFFFFu) > 2 ||
+                __builtin_popcount((uint32_t)(cand >> 16) & 0xFFFFu) > 2) {
+                // many: sort the tile's candidates and merge them in at once
+                const unsigned long long srt = row_sort16(is_cand ? key : 0ull, n16);
+                dl = dlist_merge(dl, key_dpp<0x140>(srt), lane);      // row_mirror: rank 15-j
+                cand = 0ull;
+            }
+            while (cand) {
+                const uint32_t m0 = (uint32_t)cand & 0xFFFFu;
+                const uint32_t m1 = (uint32_t)(cand >> 16) & 0xFFFFu;
+                const unsigned long long k0 = key_readlane(key, m0 ? __builtin_ctz(m0) : 0);
+                const unsigned long long k1 = key_readlane(key, m1 ? 16 + __builtin_ctz(m1) : 16);
+                const bool in0 = lane < 16, in1 = lane >= 16 && lane < 32;
+                const unsigned long long kk = in0 ? k0 : k1;
+                const unsigned long long nd = dlist_insert(dl, kk);
+                dl = ((in0 && m0) || (in1 && m1)) ? nd : dl;
+                cand &= ~((unsigned long long)(m0 & (0u - m0)) | ((unsigned long long)(m1 & (0u - m1)) << 16));
             }
         }
     };
@@ -655,11 +762,9 @@ verify_kernel(Args a)
         }
     }
     if constexpr (kTopK > 0) {
-        // the 16 lanes of a token merge their lists; lane n16 = j publishes
-        // the j-th key of the workgroup's top-k
-        const unsigned long long mine = merge_lists<16, kTopK>(tk, n16);
+        // lane n16 = j publishes the rank-j key of the workgroup's list
         if (rlane && n16 < kTopK)
-            __hip_atomic_store(&a.part_topk[((size_t)b * M + rtok) * kTopK + n16], mine,
+            __hip_atomic_store(&a.part_topk[((size_t)b * M + rtok) * kTopK + n16], dl,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     // Publication without device-scope fences: a fence here writes back and
@@ -687,9 +792,7 @@ verify_kernel(Args a)
         // Two levels, so that most of the merging overlaps the weight stream
         // of the workgroups still running: the last workgroup of each group
         // of 16 merges the group's lists into one, and the last group to
-        // finish runs the final merge.  32 threads per token; each holds a
-        // presorted chunk of kTopK/2 keys (half of one list).
-        constexpr int kE = kTopK / 2;
+        // finish runs the final merge.
         const int grp = b / 16;
         const int gsz = min(16, G - 16 * grp);
         const int n_grp = (G + 15) / 16;
@@ -702,18 +805,11 @@ verify_kernel(Args a)
         if (!s_last)
             return;
         {
-            const int m = threadIdx.x >> 5, slot = threadIdx.x & 31;
-            const int mm = m < M ? m : M - 1;
-            const int w = (slot * kE) / kTopK, off = (slot * kE) % kTopK;
-            unsigned long long ck[kE];
-#pragma unroll
-            for (int e = 0; e < kE; ++e)
-                ck[e] = w < gsz ? __hip_atomic_load(&a.part_topk[((size_t)(16 * grp + w) * M + mm) * kTopK + off + e],
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                : 0ull;
-            const unsigned long long mine = merge_lists<32, kTopK>(ck, slot);
-            if (m < M && slot < kTopK)
-                __hip_atomic_store(&a.group_topk[((size_t)grp * M + m) * kTopK + slot], mine,
+            const unsigned long long mine = merge_topk_lists<kTopK>(a.part_topk + (size_t)16 * grp * M * kTopK,
+                                                                    gsz, M, lane);
+            const int m = 2 * wave + (lane >> 5);
+            if (m < M && ((lane >> 4) & 1) == 0 && n16 < kTopK)
+                __hip_atomic_store(&a.group_topk[((size_t)grp * M + m) * kTopK + n16], mine,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -818,43 +914,32 @@ verify_kernel(Args a)
             a.n_acc[req] = n;
         }
     } else {
-        // Sampled epilogue, final merge over the group lists (32 threads
-        // per token, a presorted half list each), then the token's target
-        // probability of its draft from the k logits (top-k sampling at
-        // temperature tau), in the same order on every call.
-        constexpr int kE = kTopK / 2;
-        const int m = threadIdx.x >> 5;
-        const int slot = threadIdx.x & 31;
-        const int mm = m < M ? m : M - 1;
+        // Sampled epilogue, final merge over the group lists, then the
+        // token's target probability of its draft from the k logits (top-k
+        // sampling at temperature tau): lane j of the token's first 16-lane
+        // group holds rank j; sums are fixed butterflies over the 16 lanes.
         const int n_grp = (G + 15) / 16;
-        const int w = (slot * kE) / kTopK, off = (slot * kE) % kTopK;
-        unsigned long long ck[kE];
-#pragma unroll
-        for (int e = 0; e < kE; ++e)
-            ck[e] = w < n_grp ? __hip_atomic_load(&a.group_topk[((size_t)w * M + mm) * kTopK + off + e],
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                              : 0ull;
+        const unsigned long long mine = merge_topk_lists<kTopK>(a.group_topk, n_grp, M, lane);
+        const int m = 2 * wave + (lane >> 5);
+        const int slot = lane & 31;                   // 0..15: first group of the token
+        const int mm = m < M ? m : M - 1;
         const int T = a.T;
         const int req = mm / T, t = mm % T;
         const bool drafted = t < T - 1;
         const int d = drafted ? s_draft[req * (T - 1) + t] : -1;
-        float lmax = 0.0f, sum = 0.0f, e_d = 0.0f;
-        for (int j = 0; j < a.top_k; ++j) {
-            const unsigned long long h = group_max<32>(ck[0]);
-            if (ck[0] == h)
-                topk_pop(ck);
-            const float hv = key_value(h);
-            const int hi = key_index(h);
-            if (j == 0)
-                lmax = hv;
-            const float e = expf((hv - lmax) / a.tau);
-            sum += e;
-            if (hi == d)
-                e_d = e;
-            if (slot == j && m < M) {
-                a.topk_ids[m * a.top_k + j] = hi;
-                a.topk_logits[m * a.top_k + j] = hv;
-            }
+        const float hv = key_value(mine);
+        const int hi = key_index(mine);
+        const float lmax = key_value(key_shfl(mine, lane & ~15));
+        const float e = n16 < a.top_k ? expf((hv - lmax) / a.tau) : 0.0f;
+        float sum = e, e_d = (n16 < a.top_k && hi == d) ? e : 0.0f;
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {
+            sum += __shfl_xor(sum, off);
+            e_d += __shfl_xor(e_d, off);
+        }
+        if (slot < a.top_k && m < M) {
+            a.topk_ids[m * a.top_k + slot] = hi;
+            a.topk_logits[m * a.top_k + slot] = hv;
         }
         if (slot == 0 && m < M) {
             int ok = 0;
