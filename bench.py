@@ -108,6 +108,22 @@ def roofline(cfg, t_launch, gbs, key=None):
             "weight_gb_s": round(gbs, 2)}
 
 
+CALIBRATION_COPY_BYTES = 388_956_160   # the packed full-vocabulary head
+
+
+def calibration_copy(torch, dev):
+    """Three device copies of a known number of bytes, to scale hardware byte
+    counters (FETCH_SIZE / WRITE_SIZE) taken in the same process."""
+    src = torch.empty(CALIBRATION_COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration: 3 device copies of {CALIBRATION_COPY_BYTES} bytes")
+    del src, dst
+
+
 REQUANT = dict(V=151936, H=5120, N=4096)
 
 
@@ -129,6 +145,8 @@ def bench_requant(args):
     W = torch.from_numpy(inp["W"].view(np.int16)).view(torch.float16).to(dev)
     acts = torch.from_numpy(inp["acts"].view(np.int16)).view(torch.float16).to(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
 
     # parity gate: scales and 256 sampled packed rows against the oracle
     from oracle import requant as rq
@@ -203,6 +221,81 @@ def bench_requant(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_context_copy(args):
+    """The context-copy drafter on the workload of the wide verify block: a
+    25,000-token synthetic prompt per request, a 16-token key whose tail
+    quotes the prompt, 8 proposed tokens (verify positions 7-14).  One step
+    is one drafter call; timed for 1 request (value) and for 64."""
+    import torch
+    from int4_output_head_amd import binding
+
+    dev = torch.device("cuda:0")
+    binding.load_library()
+    from oracle import context_copy as cc
+    L, n_max, n_out = 25000, 16, 8
+    res = {}
+    for R in (1, 64):
+        rng = np.random.default_rng(R)
+        prompts = rng.integers(0, 151936, size=(R, L)).astype(np.int32)
+        keys = np.empty((R, n_max), np.int32)
+        for r in range(R):
+            s0 = int(rng.integers(n_max, L - n_out))
+            keys[r] = prompts[r, s0 - n_max:s0]
+        pr = torch.from_numpy(prompts.reshape(-1)).to(dev)
+        offs = torch.from_numpy(np.arange(R + 1, dtype=np.int64) * L).to(dev)
+        kt = torch.from_numpy(keys).to(dev)
+        tok, cnt, end, ln = binding.context_copy(pr, offs, kt, n_min=2, n_out=n_out)
+        torch.cuda.synchronize()
+        ok = 0
+        for r in range(min(R, 8)):
+            o = cc.propose(prompts[r], keys[r], 2, n_out)
+            ok += int(o["match_end"] == int(end[r]) and tok[r, : o["count"]].cpu().tolist() == o["tokens"].tolist())
+        for _ in range(max(args.warmup, 50)):
+            binding.context_copy(pr, offs, kt, n_min=2, n_out=n_out)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for i in range(args.steps):
+            binding.context_copy(pr, offs, kt, n_min=2, n_out=n_out, events=ev[i])
+        b1.record()
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+        res[R] = dict(us_per_call=round(b0.elapsed_time(b1) * 1e3 / args.steps, 3),
+                      kernel_us=round(float(per.mean()), 3), parity_checked=min(R, 8), parity_equal=ok)
+        log(f"context copy R={R}: {res[R]}")
+    t1 = res[1]["kernel_us"] * 1e-6
+    nbytes = L * 4 + n_max * 4 + n_out * 4
+    gbs = nbytes / t1 / 1e9
+    t0 = time.perf_counter()
+    rng = np.random.default_rng(5)
+    p = rng.integers(0, 151936, size=L)
+    n_cpu = 20
+    for _ in range(n_cpu):
+        cc.propose(p, p[1000:1016], 2, n_out)
+    t_cpu = (time.perf_counter() - t0) / n_cpu
+    result = {
+        "metric": "context-copy drafter: proposals per second (8 tokens from a 25k-token prompt)",
+        "value": round(1.0 / (res[1]["us_per_call"] * 1e-6), 1), "unit": "proposals/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res[1]["us_per_call"] / 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i32",
+        "data": "synthetic",
+        "config": {"workload": f"prompt lookup over a {L}-token prompt, key {n_max}, {n_out} proposed",
+                   "L": L, "n_max": n_max, "n_out": n_out, "timing": "eager, HIP events"},
+        "batch_64_requests": {"us_per_call": res[64]["us_per_call"], "kernel_us": res[64]["kernel_us"],
+                              "proposals_per_s": round(64 / (res[64]["us_per_call"] * 1e-6), 1)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 6), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "note": "one request reads 100 KB: launch and latency bound"},
+        "parity_gate": {R: {"checked": v["parity_checked"], "equal": v["parity_equal"]} for R, v in res.items()},
+        "cpu_baseline": {"value": round(1.0 / t_cpu, 2), "unit": "proposals/s", "cores": 1, "kind": "oracle",
+                         "sample": f"{n_cpu} oracle proposals over one {L}-token prompt (numpy, one thread)"},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -226,6 +319,9 @@ def main():
 
     if args.config == "requant":
         bench_requant(args)
+        return
+    if args.config == "context_copy":
+        bench_context_copy(args)
         return
 
     import torch
@@ -265,14 +361,7 @@ def main():
         log("no stored oracle argmax for this config: drafts are not aligned with the target")
 
     if args.calibrate_copy:
-        src = torch.empty(cfg.weight_bytes, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration: 3 device copies of {cfg.weight_bytes} bytes")
-        del src, dst
+        calibration_copy(torch, dev)
 
     work = binding.Workspace(binding.workspace_bytes(cfg.R, cfg.T, cfg.V, cfg.H), dev)
     stream = torch.cuda.current_stream(dev)

@@ -7,7 +7,7 @@ this package loads nothing; the library is loaded on the first call.
 
 __all__ = ["verify", "verify_batch", "verify_mapped", "verify_sampled", "check_weights", "check_vocab_map",
            "workspace_bytes", "load_library",
-           "requant_amax", "requant_scales", "requant_pack", "requantize"]
+           "requant_amax", "requant_scales", "requant_pack", "requantize", "context_copy"]
 
 
 def __getattr__(name):

@@ -63,6 +63,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                         ctypes.c_float, P, P, P, P, P, P, P, sz, P,
                                                         P, P]
         L.verify_lm_head_int4_sampled_timed.restype = i32
+        # context-copy drafter (include/int4vh_drafter.h)
+        L.context_copy_propose.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P]
+        L.context_copy_propose.restype = i32
+        L.context_copy_propose_timed.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P, P, P]
+        L.context_copy_propose_timed.restype = i32
         # offline requantisation (include/int4vh_requant.h)
         L.requant_lm_head_int4_amax.argtypes = [P, i32, i32, i32, P, i32, P]
         L.requant_lm_head_int4_amax.restype = i32
@@ -468,3 +473,36 @@ def requantize(W, acts):
     if st != OK:
         _raise(st, "requant_lm_head_int4")
     return packed, scales, amax
+
+
+# ---------------------------------------------------------------- context-copy drafter
+
+def context_copy(prompts, offsets, keys, *, n_min: int = 1, n_out: int = 8, events=None):
+    """Propose the tokens copied from each request's prompt.  prompts: int32
+    [total] (all prompts back to back); offsets: int64 [R+1]; keys: int32
+    [R, n_max] (the last n_max tokens of each sequence).  Returns (tokens
+    int32 [R, n_out] (-1 past count), count [R], match_end [R], match_len
+    [R])."""
+    _check(prompts, "prompts", torch.int32, 1)
+    _check(offsets, "offsets", torch.int64, 1)
+    _check(keys, "keys", torch.int32, 2)
+    R, n_max = keys.shape
+    if offsets.shape[0] != R + 1:
+        raise ValueError("offsets must hold R+1 values")
+    dev = prompts.device
+    tok = torch.empty((R, n_out), dtype=torch.int32, device=dev)
+    cnt = torch.empty(R, dtype=torch.int32, device=dev)
+    end = torch.empty(R, dtype=torch.int32, device=dev)
+    ln = torch.empty(R, dtype=torch.int32, device=dev)
+    L = load_library()
+    args = (_ptr(prompts), _ptr(offsets), R, _ptr(keys), n_max, n_min, n_out, _ptr(tok), _ptr(cnt),
+            _ptr(end), _ptr(ln), _stream_ptr(dev))
+    if events is None:
+        st = L.context_copy_propose(*args)
+    else:
+        stream = torch.cuda.current_stream(dev)
+        st = L.context_copy_propose_timed(*args, _event_handle(events[0], stream),
+                                          _event_handle(events[1], stream))
+    if st != OK:
+        _raise(st, "context_copy_propose")
+    return tok, cnt, end, ln

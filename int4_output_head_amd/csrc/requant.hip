@@ -13,9 +13,10 @@
 //
 //  amax_kernel   column maxima of |acts| [N, H]: a workgroup owns a strip of
 //      512 channels (16 bytes = 8 channels per lane, 1 KB per wave
-//      instruction) and 32 rows; its 4 waves take every fourth row, combine
+//      instruction) and 256 rows; its 4 waves take every fourth row, combine
 //      in LDS, and merge into the float32 maxima with an integer atomic
-//      maximum (non-negative binary32 values order like their bit patterns).
+//      maximum (non-negative binary32 values order like their bit patterns);
+//      one atomic per channel and workgroup (each costs a 32-byte write).
 //
 //  scales_kernel amax / 7 in binary32, rounded to binary16.
 //
@@ -57,7 +58,7 @@ using int4vh_detail::hip_fail;
 constexpr int kAmaxThreads = 256;               // 4 waves
 constexpr int kAmaxWaves = kAmaxThreads / 64;
 constexpr int kAmaxStrip = 64 * 8;              // channels per workgroup strip
-constexpr int kAmaxRows = 32;                   // calibration rows per workgroup
+constexpr int kAmaxRows = 256;                  // calibration rows per workgroup
 constexpr int kPackThreads = 256;               // 4 waves
 constexpr int kPackLoads = 2;                   // 16-byte loads per lane and step
 constexpr int kPackWavesPerCU = 16;             // waves per compute unit (measured best)

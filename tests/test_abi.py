@@ -51,6 +51,7 @@ def test_header_declares_expected_api():
               "verify_lm_head_int4_last_error", "verify_lm_head_int4_mapped",
               "verify_lm_head_int4_check_vocab_map", "verify_lm_head_int4_sampled",
               "verify_lm_head_int4_sampled_timed",
+              "context_copy_propose", "context_copy_propose_timed",
               "requant_lm_head_int4_amax",
               "requant_lm_head_int4_scales", "requant_lm_head_int4_pack",
               "requant_lm_head_int4_pack_timed", "requant_lm_head_int4"):
@@ -219,3 +220,25 @@ def test_sampled_rejects_invalid_arguments(lib):
     assert scall(R=2, T=9) == EUNSUPPORTED            # more than 16 rows
     assert scall(R=1, T=17) == EINVAL
     assert scall(ws_bytes=100) == EWORKSPACE
+
+
+def test_context_copy_rejects_invalid_arguments(lib):
+    P, i32 = ctypes.c_void_p, ctypes.c_int
+    f = lib.context_copy_propose
+    f.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P]
+    a = P(A)
+
+    def ccall(R=2, n_max=16, n_min=2, n_out=8, pr=A, off=A, keys=A, tok=A):
+        return f(P(pr), P(off), R, P(keys), n_max, n_min, n_out, P(tok), a, a, a, None)
+
+    assert ccall(R=0) == EINVAL
+    assert ccall(n_max=0) == EINVAL
+    assert ccall(n_max=65) == EINVAL
+    assert ccall(n_min=0) == EINVAL
+    assert ccall(n_min=17) == EINVAL
+    assert ccall(n_out=0) == EINVAL
+    assert ccall(n_out=65) == EINVAL
+    assert ccall(pr=0) == EINVAL
+    assert ccall(tok=0) == EINVAL
+    assert ccall(off=A + 4) == EALIGN
+    assert ccall(keys=A + 2) == EALIGN
