@@ -66,10 +66,14 @@ def cpu_baseline(cfg, head, trials, n_threads):
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_094_067, write=73_933,
-                     source_sha256="417cc79d8d67931dc0ed1fe3c72bbfff43f004c45622ea1dac443c7b01f7833f"),
-    "batch": dict(read=684_024_422, write=9_736_499,
-                  source_sha256="417cc79d8d67931dc0ed1fe3c72bbfff43f004c45622ea1dac443c7b01f7833f"),
+    "full_t16": dict(read=391_044_069, write=73_920, source="int4vh.hip",
+                     source_sha256="0a911c1a2ff4a95023d5494cef082af80b91cfa7e96587f3752d8af487809406"),
+    "full_t16_top16": dict(read=391_662_689, write=634_112, source="int4vh.hip",
+                           source_sha256="0a911c1a2ff4a95023d5494cef082af80b91cfa7e96587f3752d8af487809406"),
+    "batch": dict(read=683_956_086, write=9_736_480, source="int4vh.hip",
+                  source_sha256="0a911c1a2ff4a95023d5494cef082af80b91cfa7e96587f3752d8af487809406"),
+    "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
+                    source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
 
 
@@ -78,7 +82,7 @@ def measured_traffic(key, t_launch):
     rec = MEASURED_TRAFFIC.get(key)
     if rec is None:
         return None, None
-    src = os.path.join(ROOT, "int4_output_head_amd", "csrc", "int4vh.hip")
+    src = os.path.join(ROOT, "int4_output_head_amd", "csrc", rec["source"])
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
             return None, None
@@ -202,7 +206,9 @@ def bench_requant(args):
                            "p50": round(np.percentile(per_k, 50) * 1e3, 3),
                            "p90": round(np.percentile(per_k, 90) * 1e3, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("requant", t_launch)[0],
+                     "traffic_bytes_per_launch": measured_traffic("requant", t_launch)[1],
                      "algorithmic_bytes_per_launch": pack_bytes},
         "parity_gate": gate,
     }
