@@ -39,18 +39,27 @@ def stored_argmax(name):
         return json.load(f)
 
 
-def cpu_baseline(cfg, head, trials, n_threads):
+def cpu_baseline(cfg, head, trials, n_threads, top_k=0, temperature=1.0, vmap=None):
     """The oracle, as it is, on this host: whole verify steps of the same
-    workload (bounded number of trials)."""
-    from oracle import oracle
+    workload (bounded number of trials) -- the sampled oracle for top-k
+    sampling, the draft-vocabulary oracle for a mapped head."""
+    from oracle import oracle, sampled, vocab_map
     from int4_output_head_amd import synth
     times = []
     for trial in trials:
         x = synth.make_hidden(cfg, trial)
         drafts = np.zeros((cfg.R, cfg.T - 1), np.int32)
         t0 = time.perf_counter()
-        oracle.verify(x, head["packed"], head["scales"], drafts, cfg.R, cfg.T, cfg.V, cfg.H,
-                      n_threads=n_threads)
+        if top_k:
+            ones = np.ones((cfg.R, cfg.T - 1))
+            sampled.verify_sampled(x, head["packed"], head["scales"], drafts, ones, ones * 0.5, cfg.R,
+                                   cfg.T, cfg.V, cfg.H, top_k, temperature, n_threads=n_threads)
+        elif vmap is not None:
+            vocab_map.verify_mapped(x, head["packed"], head["scales"], vmap, drafts, cfg.R, cfg.T,
+                                    cfg.V, cfg.H, n_threads=n_threads)
+        else:
+            oracle.verify(x, head["packed"], head["scales"], drafts, cfg.R, cfg.T, cfg.V, cfg.H,
+                          n_threads=n_threads)
         times.append(time.perf_counter() - t0)
     t = float(np.mean(times))
     return dict(value=round(cfg.weight_bytes / t / 1e9, 4), unit="GB/s", cores=n_threads,
@@ -555,7 +564,9 @@ def main():
     if not args.no_cpu_baseline:
         n_threads = min(16, os.cpu_count() or 1)
         log(f"cpu baseline: oracle on {n_threads} threads, {args.cpu_trials} trials")
-        result["cpu_baseline"] = cpu_baseline(cfg, head, list(range(args.cpu_trials)), n_threads)
+        result["cpu_baseline"] = cpu_baseline(cfg, head, list(range(args.cpu_trials)), n_threads,
+                                              top_k=args.top_k, temperature=args.temperature,
+                                              vmap=vmap_np)
     print(json.dumps(result), flush=True)
 
 
