@@ -167,19 +167,23 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
                                int32_t *n_accepted, float *logits_out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
-/* Sampled (non-greedy) verification: the verify call with a top-k sampling
+/* Sampled (non-greedy) verification: the verify call with a sampling
  * epilogue fused into the same weight stream, for one block of R*T <= 16
  * rows (R requests of T positions).  The int4 head suffices because top-k
  * sampling needs only the ordering of the logits ("HyperQwen: 1,000 tok/s on
  * a Single RTX 3090 Through Aggressive Recurrent-State Speculation",
  * Technical Insight, lm_head paragraph).  Per row r:
- *   topk_ids[r, j], topk_logits[r, j]  the top_k largest logits, best first
- *                  (equal logits: lower row first), j < top_k <= 16
- *   argmax_ids[r], logits_max[r]        the greedy outputs, = entry 0
+ *   lse[r]         log sum_v exp(logit[r, v] / temperature) over the whole
+ *                  vocabulary (optional output, NULL to skip)
+ *   topk_ids[r, j], topk_logits[r, j]  for top_k >= 1: the top_k largest
+ *                  logits, best first (equal logits: lower row first)
+ *   argmax_ids[r], logits_max[r]        the greedy outputs
  * and per drafted position t < T-1 of request i, with d = draft_ids[i, t]:
- *   p_draft[i, t]  target probability of d under top-k sampling at
- *                  `temperature`: exp(l_d / tau) / sum_j exp(l_j / tau) over
- *                  the k logits (0 if d is not among them), in binary32
+ *   p_draft[i, t]  the target probability of d: for top_k >= 1, top-k
+ *                  sampling, exp(l_d / tau) / sum_j exp(l_j / tau) over the k
+ *                  logits (0 if d is not among them); for top_k == 0,
+ *                  sampling over the whole vocabulary, exp(l_d / tau - lse)
+ *                  (0 if d is outside [0, V)); binary32
  *   accepted       uniforms[i, t] * draft_probs[i, t] < p_draft[i, t]
  *                  (draft_probs: the drafter's probability of d, 1 for a
  *                  token copied from the context; uniforms in [0, 1) drawn
@@ -188,15 +192,16 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
  *                  sampling; the caller draws the replacement or bonus token
  *                  from the top-k outputs).
  * draft_probs, uniforms, p_draft: device float32 [R, T-1] (may be NULL only
- * when T == 1); topk_ids int32 / topk_logits float32 [R*T, top_k].
+ * when T == 1); topk_ids int32 / topk_logits float32 [R*T, top_k] (may be
+ * NULL when top_k == 0); lse float32 [R*T] or NULL.
  * Errors as verify_lm_head_int4_batch, plus INT4VH_EINVAL for top_k outside
- * [1, min(16, V)], a temperature that is not finite and > 0, or a missing
+ * [0, min(16, V)], a temperature that is not finite and > 0, or a missing
  * sampled buffer, and INT4VH_EUNSUPPORTED for R*T > 16. */
 int verify_lm_head_int4_sampled(const void *hidden, const uint8_t *packed_w, const void *scales,
                                 const int32_t *draft_ids, const float *draft_probs,
                                 const float *uniforms, int R, int T, int V, int H, int top_k,
                                 float temperature, float *logits_max, int32_t *argmax_ids,
-                                int32_t *topk_ids, float *topk_logits, float *p_draft,
+                                int32_t *topk_ids, float *topk_logits, float *lse, float *p_draft,
                                 int32_t *n_accepted, void *workspace, size_t workspace_bytes,
                                 void *stream);
 
@@ -208,9 +213,9 @@ int verify_lm_head_int4_sampled_timed(const void *hidden, const uint8_t *packed_
                                       const float *draft_probs, const float *uniforms, int R, int T,
                                       int V, int H, int top_k, float temperature,
                                       float *logits_max, int32_t *argmax_ids, int32_t *topk_ids,
-                                      float *topk_logits, float *p_draft, int32_t *n_accepted,
-                                      void *workspace, size_t workspace_bytes, void *stream,
-                                      void *event_before, void *event_after);
+                                      float *topk_logits, float *lse, float *p_draft,
+                                      int32_t *n_accepted, void *workspace, size_t workspace_bytes,
+                                      void *stream, void *event_before, void *event_after);
 
 /* Count the positions i of a row -> token map (device int32 [V]) where it is
  * not strictly increasing and non-negative (vocab_ids[0] < 0, or

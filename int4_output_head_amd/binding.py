@@ -57,11 +57,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.verify_lm_head_int4_check_vocab_map.argtypes = [P, i32, P, P]
         L.verify_lm_head_int4_check_vocab_map.restype = i32
         L.verify_lm_head_int4_sampled.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
-                                                  ctypes.c_float, P, P, P, P, P, P, P, sz, P]
+                                                  ctypes.c_float, P, P, P, P, P, P, P, P, sz, P]
         L.verify_lm_head_int4_sampled.restype = i32
         L.verify_lm_head_int4_sampled_timed.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
-                                                        ctypes.c_float, P, P, P, P, P, P, P, sz, P,
-                                                        P, P]
+                                                        ctypes.c_float, P, P, P, P, P, P, P, P, sz,
+                                                        P, P, P]
         L.verify_lm_head_int4_sampled_timed.restype = i32
         # context-copy drafter (include/int4vh_drafter.h)
         L.context_copy_propose.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P]
@@ -254,13 +254,17 @@ def verify_mapped(hidden, packed_w, scales, vocab_ids, draft_ids=None, *, R: int
 
 def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, uniforms=None, *,
                    top_k: int, temperature: float = 1.0, R: int | None = None,
-                   workspace: Workspace | None = None, events=None):
-    """Sampled verification (top-k sampling at a temperature) for R*T <= 16
-    rows.  hidden: float16 [R, T, H] (or [R*T, H] with R); draft_ids int32,
-    draft_probs and uniforms float32, each [R, T-1] (None when T == 1).
+                   workspace: Workspace | None = None, events=None, want_lse: bool = False):
+    """Sampled verification for R*T <= 16 rows: top-k sampling at a
+    temperature (top_k >= 1) or sampling over the whole vocabulary
+    (top_k == 0).  hidden: float16 [R, T, H] (or [R*T, H] with R); draft_ids
+    int32, draft_probs and uniforms float32, each [R, T-1] (None when T == 1).
     Returns (logits_max [R*T], argmax_ids [R*T], topk_ids [R*T, k],
-    topk_logits [R*T, k], p_draft [R, T-1], n_accepted [R]).  events=(before,
-    after) are recorded right around the main verify kernel."""
+    topk_logits [R*T, k], p_draft [R, T-1], n_accepted [R], lse [R*T]) (the
+    top-k outputs are None when top_k == 0; lse, the log-sum-exp of
+    logit / temperature over the vocabulary, is None unless want_lse or
+    top_k == 0).  events=(before, after) are recorded right around the main
+    verify kernel."""
     if hidden.dim() == 3:
         R, T, H = hidden.shape
         hidden = hidden.reshape(R * T, H)
@@ -290,8 +294,9 @@ def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, u
     k = int(top_k)
     lmax = torch.empty(M, dtype=torch.float32, device=dev)
     amax = torch.empty(M, dtype=torch.int32, device=dev)
-    tids = torch.empty((M, max(k, 1)), dtype=torch.int32, device=dev)
-    tlog = torch.empty((M, max(k, 1)), dtype=torch.float32, device=dev)
+    tids = torch.empty((M, k), dtype=torch.int32, device=dev) if k > 0 else None
+    tlog = torch.empty((M, k), dtype=torch.float32, device=dev) if k > 0 else None
+    lse = torch.empty(M, dtype=torch.float32, device=dev) if (want_lse or k == 0) else None
     pdr = torch.empty((R, max(T - 1, 1)), dtype=torch.float32, device=dev)
     nacc = torch.empty(R, dtype=torch.int32, device=dev)
     L = load_library()
@@ -301,7 +306,7 @@ def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, u
     ws = workspace if workspace is not None else _default_workspace(dev, need)
     args = (_ptr(hidden), _ptr(packed_w), _ptr(scales), _ptr(draft_ids), _ptr(draft_probs),
             _ptr(uniforms), R, T, V, H, k, float(temperature), _ptr(lmax), _ptr(amax), _ptr(tids),
-            _ptr(tlog), _ptr(pdr), _ptr(nacc), _ptr(ws.tensor), ws.nbytes, _stream_ptr(dev))
+            _ptr(tlog), _ptr(lse), _ptr(pdr), _ptr(nacc), _ptr(ws.tensor), ws.nbytes, _stream_ptr(dev))
     if events is None:
         st = L.verify_lm_head_int4_sampled(*args)
     else:
@@ -310,7 +315,7 @@ def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, u
                                                  _event_handle(events[1], stream))
     if st != OK:
         _raise(st, "verify_lm_head_int4_sampled")
-    return lmax, amax, tids, tlog, pdr[:, : max(T - 1, 0)], nacc
+    return lmax, amax, tids, tlog, pdr[:, : max(T - 1, 0)], nacc, lse
 
 
 def check_vocab_map(vocab_ids) -> torch.Tensor:

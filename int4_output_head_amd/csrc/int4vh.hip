@@ -104,7 +104,9 @@ constexpr int kBatchMaxRows = 4096;       // rows per launch of the batch path
 constexpr size_t kWsTicket = 0;                                   // uint32 ticket
 constexpr size_t kWsKeys = 256;                                   // uint64 [4096] batch winner keys
 constexpr size_t kWsGroupTk = kWsKeys + (size_t)kBatchMaxRows * 8;   // uint32 [64] group tickets
-constexpr size_t kWsCtlBytes = kWsGroupTk + 256;
+constexpr size_t kWsDraftSeen = kWsGroupTk + 256;                     // int32 [16] draft logit written
+constexpr size_t kWsDraftLogit = kWsDraftSeen + 64;                   // float [16] the draft's logit
+constexpr size_t kWsCtlBytes = kWsGroupTk + 512;
 constexpr size_t kWsExp = kWsCtlBytes;                            // int32 [4096] step exponents
 constexpr size_t kWsPart = kWsExp + (size_t)kBatchMaxRows * 4;    // uint64 [kMaxGrid][16]
 constexpr size_t kWsFrag = kWsPart + (size_t)kMaxGrid * kMaxRows * 8;   // activation fragments
@@ -113,7 +115,9 @@ constexpr int kMaxTopK = 16;              // largest k of the sampled epilogue
 constexpr int kSampledMaxGrid = 256;      // workgroups of a sampled call (16 groups of 16)
 constexpr size_t kWsTopK = kWsFrag + kFragBytes;                  // uint64 [256][16][kMaxTopK]
 constexpr size_t kWsGroupTopK = kWsTopK + (size_t)kSampledMaxGrid * kMaxRows * kMaxTopK * 8;
-constexpr size_t kWsBytes = kWsGroupTopK + (size_t)(kSampledMaxGrid / 16) * kMaxRows * kMaxTopK * 8;
+constexpr size_t kWsLse = kWsGroupTopK + (size_t)(kSampledMaxGrid / 16) * kMaxRows * kMaxTopK * 8;
+constexpr size_t kWsGroupLse = kWsLse + (size_t)kSampledMaxGrid * kMaxRows * 8;   // (m, s) pairs
+constexpr size_t kWsBytes = kWsGroupLse + (size_t)(kSampledMaxGrid / 16) * kMaxRows * 8;
 static_assert(kWsCtlBytes % 256 == 0 && kWsExp % 256 == 0 && kWsPart % 256 == 0 &&
                   kWsFrag % 256 == 0 && kWsTopK % 256 == 0 && kWsGroupTopK % 256 == 0,
               "workspace regions stay 256-byte aligned");
@@ -177,9 +181,14 @@ struct Args {
     float tau;                // temperature > 0
     const float *dprob;       // [R, T-1] drafter probability of each draft
     const float *unif;        // [R, T-1] uniforms in [0, 1)
-    int32_t *topk_ids;        // [M, k]
+    int32_t *topk_ids;        // [M, k] (unused when top_k == 0)
     float *topk_logits;       // [M, k]
     float *p_draft;           // [R, T-1]
+    float *lse_out;           // [M] log sum exp(logit / tau), or null
+    uint64_t *part_lse;       // [grid, M] per-workgroup (max, sum) of exp2 terms
+    uint64_t *group_lse;      // [grid / 16, M]
+    int32_t *draft_seen;      // [16] set when the draft's logit was written; zero between calls
+    float *draft_logit;       // [16]
     uint32_t *ticket;
     int32_t *exps;            // [16]
     const u32x4 *frag;        // activation fragments
@@ -331,6 +340,24 @@ __device__ __forceinline__ unsigned long long dlist_merge(unsigned long long a, 
     return key_cex<1>(key_cex<2>(key_cex<4>(key_cex<8>(c, j, (j & 8) == 0), j, (j & 4) == 0), j,
                                  (j & 2) == 0),
                       j, (j & 1) == 0);
+}
+
+// Running sums of exp2 terms, (m, s) = (maximum exponent, sum of
+// exp2(z - m)); an empty pair is (-inf, 0).  Combination scales each sum to
+// the larger maximum (factor 1 when the maxima are equal, including two
+// empty pairs).
+__device__ __forceinline__ void lse_combine(float &m, float &s, float mo, float so)
+{
+    const float mn = fmaxf(m, mo);
+    const float f1 = m == mn ? 1.0f : __builtin_amdgcn_exp2f(m - mn);
+    const float f2 = mo == mn ? 1.0f : __builtin_amdgcn_exp2f(mo - mn);
+    s = s * f1 + so * f2;
+    m = mn;
+}
+
+__device__ __forceinline__ uint64_t lse_pack(float m, float s)
+{
+    return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)__float_as_uint(m);
 }
 
 // Merge up to 16 published top-k lists ([n_lists][M][kTopK] keys, rank
@@ -524,11 +551,12 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
 }
 
 // ---------------------------------------------------------------- verify_kernel
-template <int kP, int kUnits, int kRing, bool kLogits, int kTopK>
+template <int kP, int kUnits, int kRing, bool kLogits, int kTopK, bool kLse>
 __global__ void __launch_bounds__(kThreads)
 verify_kernel(Args a)
 {
     static_assert(kTopK == 0 || (kTopK <= kMaxTopK && !kLogits), "sampled epilogue");
+    static_assert(!kLse || kTopK > 0, "the log-sum-exp belongs to the sampled epilogue");
     constexpr int kGroups = Slots<kP>::kGroups;
     constexpr int kTileBytes = kUnits * kWaves * 1024;     // LDS image of one tile (max H)
     // All LDS lives in one object: the weight ring, then the per-wave
@@ -630,8 +658,14 @@ verify_kernel(Args a)
     float bv = -__builtin_huge_valf();
     int bi = 0x7FFFFFFF;
     // sampled epilogue: the token's distributed top-k list (lanes 0-15: token
-    // 2*wave, lanes 16-31: token 2*wave+1; rank = n16)
+    // 2*wave, lanes 16-31: token 2*wave+1; rank = n16), the lane's running
+    // (max, sum) of exp2(logit * log2(e) / tau), and the token's draft id
     unsigned long long dl = 0ull;
+    float lm = -__builtin_huge_valf(), ls = 0.0f;
+    const float zscale = 1.4426950408889634f / a.tau;
+    int my_draft = -1;
+    if (kTopK > 0 && rlane && a.T > 1 && (rtok % a.T) < a.T - 1)
+        my_draft = a.draft[(rtok / a.T) * (a.T - 1) + rtok % a.T];
     // Rows of D that hold limbs of token t are t, t + kP, t + 2*kP (those
     // with a limb index below 3).  Every lane loads (clamped to a valid
     // token) so the loads are straight-line and all in flight together.
@@ -654,8 +688,15 @@ verify_kernel(Args a)
                     bv = val;
                     bi = v;
                 }
-                if constexpr (kTopK > 0)
+                if constexpr (kTopK > 0) {
                     key = order_key(val, v);
+                    if constexpr (kLse)
+                        lse_combine(lm, ls, val * zscale, 1.0f);
+                    if (kLse && v == my_draft) {      // one lane of one workgroup per token
+                        __hip_atomic_store(&a.draft_logit[rtok], val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&a.draft_seen[rtok], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
                 if (kLogits)
                     a.logits_out[(size_t)rtok * V + v] = val;
             }
@@ -762,10 +803,23 @@ verify_kernel(Args a)
         }
     }
     if constexpr (kTopK > 0) {
-        // lane n16 = j publishes the rank-j key of the workgroup's list
+        // lane n16 = j publishes the rank-j key of the workgroup's list;
+        // the 16 lanes' (max, sum) pairs combine (fixed butterfly) and lane
+        // 0 of the token publishes them
         if (rlane && n16 < kTopK)
             __hip_atomic_store(&a.part_topk[((size_t)b * M + rtok) * kTopK + n16], dl,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if constexpr (kLse) {
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) {
+                const float mo = __shfl_xor(lm, off);
+                const float so = __shfl_xor(ls, off);
+                lse_combine(lm, ls, mo, so);
+            }
+            if (rlane && n16 == 0)
+                __hip_atomic_store(&a.part_lse[(size_t)b * M + rtok], lse_pack(lm, ls), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     // Publication without device-scope fences: a fence here writes back and
     // invalidates the whole L2 of the XCD, which costs tens of microseconds
@@ -811,6 +865,16 @@ verify_kernel(Args a)
             if (m < M && ((lane >> 4) & 1) == 0 && n16 < kTopK)
                 __hip_atomic_store(&a.group_topk[((size_t)grp * M + m) * kTopK + n16], mine,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (kLse && m < M && (lane & 31) == 0) {
+                float gm = -__builtin_huge_valf(), gs = 0.0f;
+                for (int w = 0; w < gsz; ++w) {
+                    const uint64_t pr = __hip_atomic_load(&a.part_lse[(size_t)(16 * grp + w) * M + m],
+                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    lse_combine(gm, gs, __uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32)));
+                }
+                __hip_atomic_store(&a.group_lse[(size_t)grp * M + m], lse_pack(gm, gs), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __syncthreads();
@@ -942,14 +1006,38 @@ verify_kernel(Args a)
             a.topk_logits[m * a.top_k + slot] = hv;
         }
         if (slot == 0 && m < M) {
+            // log sum exp(logit / tau) over the whole vocabulary
+            float lse = 0.0f;
+            if constexpr (kLse) {
+                float gm = -__builtin_huge_valf(), gs = 0.0f;
+                for (int w = 0; w < n_grp; ++w) {
+                    const uint64_t pr = __hip_atomic_load(&a.group_lse[(size_t)w * M + m], __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                    lse_combine(gm, gs, __uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32)));
+                }
+                lse = (gm + __log2f(gs)) * 0.6931471805599453f;
+                if (a.lse_out)
+                    a.lse_out[m] = lse;
+            }
             int ok = 0;
             if (drafted) {
                 const int di = req * (T - 1) + t;
-                const float p = e_d / sum;
+                float p;
+                if (!kLse || a.top_k > 0) {
+                    p = e_d / sum;
+                } else {
+                    const bool seen = __hip_atomic_load(&a.draft_seen[m], __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT) != 0;
+                    p = seen ? expf(__hip_atomic_load(&a.draft_logit[m], __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) / a.tau - lse)
+                             : 0.0f;
+                }
                 a.p_draft[di] = p;
                 ok = a.unif[di] * a.dprob[di] < p;
             }
             s_accept[m] = ok;
+            if constexpr (kLse)
+                __hip_atomic_store(&a.draft_seen[m], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         if (threadIdx.x < (unsigned)a.R) {
@@ -1462,52 +1550,53 @@ struct Pair {
 };
 
 // Ring depth: three tiles in flight while they fit in LDS, else two.
-template <int kP, int kUnits, bool kLogits, int kTopK>
+template <int kP, int kUnits, bool kLogits, int kTopK, bool kLse>
 Pair make_pair()
 {
     constexpr int kRing = kUnits <= 5 ? 3 : 2;
-    return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits, kTopK>};
+    return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits, kTopK, kLse>};
 }
 
-template <int kP, bool kLogits, int kTopK>
+template <int kP, bool kLogits, int kTopK, bool kLse>
 Pair pick(int units)
 {
     switch (units) {
-    case 1: return make_pair<kP, 1, kLogits, kTopK>();
-    case 2: return make_pair<kP, 2, kLogits, kTopK>();
-    case 3: return make_pair<kP, 3, kLogits, kTopK>();
-    case 4: return make_pair<kP, 4, kLogits, kTopK>();
-    case 5: return make_pair<kP, 5, kLogits, kTopK>();
-    case 6: return make_pair<kP, 6, kLogits, kTopK>();
-    case 7: return make_pair<kP, 7, kLogits, kTopK>();
-    default: return make_pair<kP, 8, kLogits, kTopK>();
+    case 1: return make_pair<kP, 1, kLogits, kTopK, kLse>();
+    case 2: return make_pair<kP, 2, kLogits, kTopK, kLse>();
+    case 3: return make_pair<kP, 3, kLogits, kTopK, kLse>();
+    case 4: return make_pair<kP, 4, kLogits, kTopK, kLse>();
+    case 5: return make_pair<kP, 5, kLogits, kTopK, kLse>();
+    case 6: return make_pair<kP, 6, kLogits, kTopK, kLse>();
+    case 7: return make_pair<kP, 7, kLogits, kTopK, kLse>();
+    default: return make_pair<kP, 8, kLogits, kTopK, kLse>();
     }
 }
 
-template <bool kLogits, int kTopK>
+template <bool kLogits, int kTopK, bool kLse>
 Pair pick_rows(int M, int units, int *kp)
 {
     if (M <= 5) {
         *kp = 5;
-        return pick<5, kLogits, kTopK>(units);
+        return pick<5, kLogits, kTopK, kLse>(units);
     }
     if (M <= 8) {
         *kp = 8;
-        return pick<8, kLogits, kTopK>(units);
+        return pick<8, kLogits, kTopK, kLse>(units);
     }
     *kp = 16;
-    return pick<16, kLogits, kTopK>(units);
+    return pick<16, kLogits, kTopK, kLse>(units);
 }
 
-// Kernel pair for a call: greedy (with or without every logit written) or
-// the sampled epilogue with an 8- or 16-entry top-k list.
-Pair pick_kernels(int M, int units, bool logits, int top_k, int *kp)
+// Kernel pair for a call: greedy (with or without every logit written), or
+// the sampled epilogue with an 8- or 16-entry top-k list, with the running
+// log-sum-exp when the call samples over the whole vocabulary or asks for it.
+Pair pick_kernels(int M, int units, bool logits, bool sampled, int top_k, bool lse, int *kp)
 {
-    if (top_k > 8)
-        return pick_rows<false, 16>(M, units, kp);
-    if (top_k > 0)
-        return pick_rows<false, 8>(M, units, kp);
-    return logits ? pick_rows<true, 0>(M, units, kp) : pick_rows<false, 0>(M, units, kp);
+    if (sampled && top_k > 8)
+        return lse ? pick_rows<false, 16, true>(M, units, kp) : pick_rows<false, 16, false>(M, units, kp);
+    if (sampled)
+        return lse ? pick_rows<false, 8, true>(M, units, kp) : pick_rows<false, 8, false>(M, units, kp);
+    return logits ? pick_rows<true, 0, false>(M, units, kp) : pick_rows<false, 0, false>(M, units, kp);
 }
 
 // K steps of the batch path (128 channels each, rounded up to even).
@@ -1627,6 +1716,7 @@ struct Sampled {
     int32_t *topk_ids;
     float *topk_logits;
     float *p_draft;
+    float *lse;
 };
 
 int launch_verify(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
@@ -1664,6 +1754,11 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     a.topk_ids = smp ? smp->topk_ids : nullptr;
     a.topk_logits = smp ? smp->topk_logits : nullptr;
     a.p_draft = smp ? smp->p_draft : nullptr;
+    a.lse_out = smp ? smp->lse : nullptr;
+    a.part_lse = reinterpret_cast<uint64_t *>(wsb + kWsLse);
+    a.group_lse = reinterpret_cast<uint64_t *>(wsb + kWsGroupLse);
+    a.draft_seen = reinterpret_cast<int32_t *>(wsb + kWsDraftSeen);
+    a.draft_logit = reinterpret_cast<float *>(wsb + kWsDraftLogit);
     a.hidden = static_cast<const uint16_t *>(hidden);
     a.w = w;
     a.scales = static_cast<const uint16_t *>(scales);
@@ -1694,7 +1789,8 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     if (smp && grid > kSampledMaxGrid)
         grid = kSampledMaxGrid;
     int kp = 16;
-    const Pair fn = pick_kernels(a.M, units, lout != nullptr, smp ? smp->top_k : 0, &kp);
+    const Pair fn = pick_kernels(a.M, units, lout != nullptr, smp != nullptr, smp ? smp->top_k : 0,
+                                 smp && (smp->top_k == 0 || smp->lse != nullptr), &kp);
     hipLaunchKernelGGL(fn.stage, dim3(kp), dim3(kStageThreads), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess)
@@ -1784,23 +1880,24 @@ int verify_lm_head_int4_sampled_timed(const void *hidden, const uint8_t *packed_
                                       const float *draft_probs, const float *uniforms, int R, int T,
                                       int V, int H, int top_k, float temperature,
                                       float *logits_max, int32_t *argmax_ids, int32_t *topk_ids,
-                                      float *topk_logits, float *p_draft, int32_t *n_accepted,
-                                      void *workspace, size_t workspace_bytes, void *stream,
-                                      void *event_before, void *event_after)
+                                      float *topk_logits, float *lse, float *p_draft,
+                                      int32_t *n_accepted, void *workspace, size_t workspace_bytes,
+                                      void *stream, void *event_before, void *event_after)
 {
-    if (top_k < 1 || top_k > kMaxTopK || top_k > V || !(temperature > 0.0f) ||
+    if (top_k < 0 || top_k > kMaxTopK || top_k > V || !(temperature > 0.0f) ||
         !(temperature < __builtin_huge_valf()))
         return INT4VH_EINVAL;
-    if (!topk_ids || !topk_logits)
+    if (top_k > 0 && (!topk_ids || !topk_logits))
         return INT4VH_EINVAL;
     if (T > 1 && (!draft_probs || !uniforms || !p_draft))
         return INT4VH_EINVAL;
-    if (!aligned(topk_ids, 4) || !aligned(topk_logits, 4) || (draft_probs && !aligned(draft_probs, 4)) ||
+    if ((topk_ids && !aligned(topk_ids, 4)) || (topk_logits && !aligned(topk_logits, 4)) ||
+        (lse && !aligned(lse, 4)) || (draft_probs && !aligned(draft_probs, 4)) ||
         (uniforms && !aligned(uniforms, 4)) || (p_draft && !aligned(p_draft, 4)))
         return INT4VH_EALIGN;
     // (more than 16 rows: INT4VH_EUNSUPPORTED from launch_verify, after the
     // common validation)
-    const Sampled smp{top_k, temperature, draft_probs, uniforms, topk_ids, topk_logits, p_draft};
+    const Sampled smp{top_k, temperature, draft_probs, uniforms, topk_ids, topk_logits, p_draft, lse};
     return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
                          n_accepted, nullptr, workspace, workspace_bytes, stream, event_before,
                          event_after, nullptr, &smp);
@@ -1810,14 +1907,15 @@ int verify_lm_head_int4_sampled(const void *hidden, const uint8_t *packed_w, con
                                 const int32_t *draft_ids, const float *draft_probs,
                                 const float *uniforms, int R, int T, int V, int H, int top_k,
                                 float temperature, float *logits_max, int32_t *argmax_ids,
-                                int32_t *topk_ids, float *topk_logits, float *p_draft,
+                                int32_t *topk_ids, float *topk_logits, float *lse, float *p_draft,
                                 int32_t *n_accepted, void *workspace, size_t workspace_bytes,
                                 void *stream)
 {
     return verify_lm_head_int4_sampled_timed(hidden, packed_w, scales, draft_ids, draft_probs,
                                              uniforms, R, T, V, H, top_k, temperature, logits_max,
-                                             argmax_ids, topk_ids, topk_logits, p_draft, n_accepted,
-                                             workspace, workspace_bytes, stream, nullptr, nullptr);
+                                             argmax_ids, topk_ids, topk_logits, lse, p_draft,
+                                             n_accepted, workspace, workspace_bytes, stream, nullptr,
+                                             nullptr);
 }
 
 int verify_lm_head_int4_check_vocab_map(const int32_t *vocab_ids, int V, int32_t *n_bad_out,

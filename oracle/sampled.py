@@ -19,6 +19,10 @@ used (standard speculative sampling restricted to a top-k target):
     token copied from the context), is accepted when u_t * q_t < p_t(d_t),
     with u_t uniform in [0, 1) supplied by the caller; the accepted count is
     the number of leading accepted drafts (the first rejection stops);
+  * with k = 0 the target distribution is plain sampling at temperature
+    tau over the whole vocabulary: p(d) = exp(logit_d / tau - lse), where
+    lse = log sum_v exp(logit_v / tau) (ids outside the vocabulary: p = 0);
+    lse is reported for every row in both modes;
   * the replacement or bonus token is drawn by the caller from the top-k
     outputs (it needs the drafter's full distribution for the residual).
 
@@ -58,8 +62,25 @@ def draft_prob(top_ids, top_vals, d: int, tau: float) -> float:
     return float(w[hit[0]] / w.sum()) if hit.size else 0.0
 
 
-def sampled_accept(top_ids, top_vals, draft_ids, draft_probs, uniforms, R: int, T: int, tau: float):
-    """p_draft [R, T-1] and the accepted count per request."""
+def lse_rows(logits, tau: float) -> np.ndarray:
+    """log sum_v exp(logit / tau) per row, binary64, evaluated with the
+    row maximum factored out."""
+    z = np.asarray(logits, np.float64) / tau
+    m = z.max(axis=1)
+    return m + np.log(np.exp(z - m[:, None]).sum(axis=1))
+
+
+def full_softmax_prob(logit_row, lse: float, d: int, tau: float) -> float:
+    """p(d) under sampling over the whole vocabulary at temperature tau."""
+    if not 0 <= d < len(logit_row):
+        return 0.0
+    return float(np.exp(np.float64(logit_row[d]) / tau - lse))
+
+
+def sampled_accept(top_ids, top_vals, draft_ids, draft_probs, uniforms, R: int, T: int, tau: float,
+                   logits=None, lse=None):
+    """p_draft [R, T-1] and the accepted count per request: top-k sampling,
+    or with logits and lse given, sampling over the whole vocabulary."""
     n = np.zeros(R, np.int32)
     p = np.zeros((R, max(T - 1, 0)), np.float64)
     if T == 1:
@@ -69,7 +90,11 @@ def sampled_accept(top_ids, top_vals, draft_ids, draft_probs, uniforms, R: int, 
     u = np.asarray(uniforms, np.float64).reshape(R, T - 1)
     for i in range(R):
         for t in range(T - 1):
-            p[i, t] = draft_prob(top_ids[i * T + t], top_vals[i * T + t], int(d[i, t]), tau)
+            r = i * T + t
+            if logits is None:
+                p[i, t] = draft_prob(top_ids[r], top_vals[r], int(d[i, t]), tau)
+            else:
+                p[i, t] = full_softmax_prob(logits[r], lse[r], int(d[i, t]), tau)
         k = 0
         while k < T - 1 and u[i, k] * q[i, k] < p[i, k]:
             k += 1
@@ -83,7 +108,12 @@ def verify_sampled(hidden_bits, packed, scales_bits, draft_ids, draft_probs, uni
         raise ValueError("temperature must be > 0")
     lg = oracle.logits(hidden_bits, packed, scales_bits, R * T, V, H, n_threads=n_threads)
     idx, mx, gap, amax = oracle.argmax_rows(lg)
-    ids, vals = topk_rows(lg, k)
-    p, n = sampled_accept(ids, vals, draft_ids, draft_probs, uniforms, R, T, tau)
+    lse = lse_rows(lg, tau)
+    if k > 0:
+        ids, vals = topk_rows(lg, k)
+        p, n = sampled_accept(ids, vals, draft_ids, draft_probs, uniforms, R, T, tau)
+    else:
+        ids = vals = None
+        p, n = sampled_accept(None, None, draft_ids, draft_probs, uniforms, R, T, tau, logits=lg, lse=lse)
     return dict(logits=lg, logits_max=mx, argmax_ids=idx, gap=gap, amax=amax, topk_ids=ids,
-                topk_logits=vals, p_draft=p, n_accepted=n)
+                topk_logits=vals, lse=lse, p_draft=p, n_accepted=n)

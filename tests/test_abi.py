@@ -197,15 +197,18 @@ def test_requant_rejects_invalid_arguments(lib):
 def test_sampled_rejects_invalid_arguments(lib):
     P, i32 = ctypes.c_void_p, ctypes.c_int
     f = lib.verify_lm_head_int4_sampled
-    f.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, P, P, P, P, P, P, P,
+    f.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, P, P, P, P, P, P, P, P,
                   ctypes.c_size_t, P]
     a = P(A)
 
-    def scall(R=1, T=4, V=100, H=256, k=8, tau=1.0, dprob=A, unif=A, pdr=A, tids=A, tlog=A, ws_bytes=WS):
-        return f(a, a, a, a, P(dprob), P(unif), R, T, V, H, k, tau, a, a, P(tids), P(tlog), P(pdr), a,
-                 a, ws_bytes, None)
+    def scall(R=1, T=4, V=100, H=256, k=8, tau=1.0, dprob=A, unif=A, pdr=A, tids=A, tlog=A, lse=A,
+              ws_bytes=WS):
+        return f(a, a, a, a, P(dprob), P(unif), R, T, V, H, k, tau, a, a, P(tids), P(tlog), P(lse),
+                 P(pdr), a, a, ws_bytes, None)
 
-    assert scall(k=0) == EINVAL
+    assert scall(k=-1) == EINVAL
+    assert scall(k=0, tids=0, tlog=0, ws_bytes=100) == EWORKSPACE   # k = 0 needs no top-k buffers
+    assert scall(lse=A + 2) == EALIGN
     assert scall(k=17) == EINVAL
     assert scall(k=8, V=7) == EINVAL                  # k > V
     assert scall(tau=0.0) == EINVAL

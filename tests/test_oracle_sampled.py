@@ -84,3 +84,38 @@ def test_greedy_limit(oracle_mod):
         assert int(o["n_accepted"][0]) == 4
         gg = oracle_mod.verify(inp["hidden"], inp["packed"], inp["scales"], d, R, T, V, H)
         assert int(gg["n_accepted"][0]) == 4
+
+
+def test_lse_and_full_softmax_closed_forms():
+    lg = np.array([[2.0, 1.0, 0.0, -1.0]], np.float32)
+    for tau in (1.0, 0.5, 3.0):
+        lse = sm.lse_rows(lg, tau)[0]
+        want = math.log(sum(math.exp(v / tau) for v in (2.0, 1.0, 0.0, -1.0)))
+        assert lse == pytest.approx(want, rel=1e-15)
+        assert sm.full_softmax_prob(lg[0], lse, 1, tau) == pytest.approx(
+            math.exp(1.0 / tau) / sum(math.exp(v / tau) for v in (2.0, 1.0, 0.0, -1.0)), rel=1e-14)
+    assert sm.full_softmax_prob(lg[0], 0.0, 4, 1.0) == 0.0 and sm.full_softmax_prob(lg[0], 0.0, -1, 1.0) == 0.0
+    # large logits: the factored maximum keeps it finite
+    big = np.array([[1000.0, 999.0]], np.float32)
+    assert sm.lse_rows(big, 1.0)[0] == pytest.approx(1000.0 + math.log(1 + math.exp(-1)), rel=1e-15)
+    # probabilities over the whole vocabulary sum to one
+    rng = np.random.default_rng(0)
+    row = rng.normal(0, 7, size=500).astype(np.float32)
+    lse = sm.lse_rows(row[None, :], 0.8)[0]
+    assert sum(sm.full_softmax_prob(row, lse, v, 0.8) for v in range(500)) == pytest.approx(1.0, abs=1e-12)
+
+
+def test_full_softmax_acceptance_vs_topk(oracle_mod):
+    """k = 0 (the whole vocabulary) gives each draft a probability no larger
+    than top-k sampling does when the draft is among the top k."""
+    R, T, V, H = 1, 8, 400, 64
+    inp = synth.uniform_inputs(T, V, H, seed=4)
+    g = oracle_mod.verify(inp["hidden"], inp["packed"], inp["scales"], np.zeros(T - 1, np.int32), R, T, V, H)
+    d = np.asarray(g["argmax_ids"][: T - 1], np.int32)
+    q = np.ones((R, T - 1))
+    u = np.full((R, T - 1), 0.3)
+    full = sm.verify_sampled(inp["hidden"], inp["packed"], inp["scales"], d, q, u, R, T, V, H, 0, 1.0)
+    top = sm.verify_sampled(inp["hidden"], inp["packed"], inp["scales"], d, q, u, R, T, V, H, 16, 1.0)
+    assert np.all(full["p_draft"] <= top["p_draft"] + 1e-15)
+    assert full["topk_ids"] is None and full["lse"].shape == (T,)
+    assert np.allclose(full["lse"], top["lse"])
