@@ -161,6 +161,11 @@ __device__ __forceinline__ void lds_store_u64(unsigned long long *p, unsigned lo
 {
     asm volatile("ds_write_b64 %0, %1" ::"v"(lds_offset(p)), "v"(v) : "memory");
 }
+__device__ __forceinline__ void lds_store_u32(void *p, uint32_t v)
+{
+    asm volatile("ds_write_b32 %0, %1" ::"v"(lds_offset(reinterpret_cast<unsigned long long *>(p))), "v"(v)
+                 : "memory");
+}
 
 struct Args {
     const uint16_t *hidden;   // [M, H] binary16
@@ -551,12 +556,13 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
 }
 
 // ---------------------------------------------------------------- verify_kernel
-template <int kP, int kUnits, int kRing, bool kLogits, int kTopK, bool kLse>
+template <int kP, int kUnits, int kRing, bool kLogits, int kTopK, bool kLse, bool kFused>
 __global__ void __launch_bounds__(kThreads)
 verify_kernel(Args a)
 {
     static_assert(kTopK == 0 || (kTopK <= kMaxTopK && !kLogits), "sampled epilogue");
     static_assert(!kLse || kTopK > 0, "the log-sum-exp belongs to the sampled epilogue");
+    static_assert(!kFused || (kP == 5 && kTopK == 0), "fused staging: one MFMA row group, greedy");
     constexpr int kGroups = Slots<kP>::kGroups;
     constexpr int kTileBytes = kUnits * kWaves * 1024;     // LDS image of one tile (max H)
     // All LDS lives in one object: the weight ring, then the per-wave
@@ -597,19 +603,6 @@ verify_kernel(Args a)
     const int n_my = (a.n_tiles - b + G - 1) / G;
     const int chunks_per_row = H / 32;                     // 16-byte chunks per weight row
 
-    // ---------------- activation fragments and step exponents (from stage_kernel)
-    i32x4 afr[kUnits][2][kGroups];
-#pragma unroll
-    for (int i = 0; i < kUnits; ++i)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int g = 0; g < kGroups; ++g)
-                afr[i][t][g] = __builtin_bit_cast(i32x4, a.frag[frag_index<kP, kUnits>(wave, i, t, g, lane)]);
-    const int rtok = 2 * wave + ((lane >> 4) & 1);         // token reduced by this lane
-    const bool rlane = lane < 32 && rtok < M;
-    const int rexp = a.exps[rtok < M ? rtok : 0] - 4;      // weights carry a factor 16
-
     // ---------------- weight stream into the LDS ring
     // Wave w copies 1 KB blocks jj = w*kUnits + m of the tile (m < kUnits);
     // lane l of a block fetches chunk l ^ (jj & 7) so that LDS holds the
@@ -630,10 +623,155 @@ verify_kernel(Args a)
                                              (lds_void *)(dst + jj * 1024), 16, 0, INT4VH_WEIGHT_AUX);
         }
     };
+    // ---------------- activation fragments and step exponents
+    const int rtok = 2 * wave + ((lane >> 4) & 1);         // token reduced by this lane
+    const bool rlane = lane < 32 && rtok < M;
+    i32x4 afr[kUnits][2][kGroups];
+    int rexp;
+    if constexpr (!kFused) {
+        // from stage_kernel, in the workspace
 #pragma unroll
-    for (int k = 0; k < kRing - 1; ++k)
-        if (k < n_my)
+        for (int i = 0; i < kUnits; ++i)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int g = 0; g < kGroups; ++g)
+                    afr[i][t][g] = __builtin_bit_cast(i32x4, a.frag[frag_index<kP, kUnits>(wave, i, t, g, lane)]);
+        rexp = a.exps[rtok < M ? rtok : 0] - 4;              // weights carry a factor 16
+#pragma unroll
+        for (int k = 0; k < kRing - 1; ++k)
+            if (k < n_my)
+                issue_tile(k);
+    } else {
+        // Staging done here for M <= 2 rows.  The scale row and the hidden
+        // rows are copied into the last ring slot (unused until the main loop
+        // refills it) with the same LDS copies as the weights, ahead of the
+        // weight prologue, so one count of outstanding copies covers both.
+        // While the weights stream, the workgroup turns the rows into codes
+        // (each wave its slice of the hidden dimension, same arithmetic as
+        // stage_kernel) in the partial-sum area of LDS (free until the main
+        // loop), and every lane reads its A fragments from there.
+        constexpr int kSliceCh = kUnits * kUnitH;           // channels of a wave's slice
+        constexpr int kHPad = kWaves * kSliceCh;              // padded hidden dimension
+        constexpr int kRowBlocks = kHPad * 2 / 1024;          // 1 KB blocks of one padded fp16 row
+        constexpr int kRounds = (kSliceCh + 511) / 512;       // 8-channel chunks per lane
+        static_assert(3 * kHPad * 2 <= kTileBytes, "scale and hidden rows fit one ring slot");
+        uint8_t *rows = s_ring[kRing - 1];                    // [scales | hidden 0 | hidden 1], kHPad each
+        uint8_t *codes = reinterpret_cast<uint8_t *>(&s_part[0][0][0][0]);     // [3][M][kHPad]
+        float *wmax = reinterpret_cast<float *>(codes + 3 * M * kHPad);      // [kWaves][2]
+        {
+            const unsigned long long row_bytes = (unsigned long long)H * 2;
+            for (int q = wave; q < (M + 1) * kRowBlocks; q += kWaves) {
+                const int arr = q / kRowBlocks;               // 0: scales, 1 + m: hidden row m
+                const unsigned long long off = (unsigned long long)(q % kRowBlocks) * 1024 + lane * 16;
+                const uint16_t *src = arr == 0 ? a.scales : a.hidden + (size_t)(arr - 1) * H;
+                // bytes past the row: clamped, masked below
+                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(src) +
+                                                     (off < row_bytes ? off : row_bytes - 16),
+                                                 (lds_void *)(rows + q * 1024), 16, 0, 0);
+            }
+        }
+        // the prologue tiles, unconditional (a tile past the head reads
+        // clamped bytes into a ring slot that is never used), so that the
+        // count below is exactly this wave's weight copies
+#pragma unroll
+        for (int k = 0; k < kRing - 1; ++k)
             issue_tile(k);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm((kRing - 1) * kUnits));
+        barrier_no_fence();
+
+        float xs[2][kRounds][8];
+        float mx[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int r = 0; r < kRounds; ++r) {
+            const int cl = 8 * lane + 512 * r;                  // channel within the slice
+            const int c0 = wave * kSliceCh + cl;
+            const bool in_slice = cl < kSliceCh;
+            const u32x4 sx = *reinterpret_cast<const u32x4 *>(rows + 2 * (in_slice ? c0 : 0));
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const bool ok = m < M && in_slice && c0 < H;
+                const u32x4 hx = *reinterpret_cast<const u32x4 *>(rows + 2 * ((1 + (m < M ? m : 0)) * kHPad +
+                                                                                (in_slice ? c0 : 0)));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t hb = (j & 1) ? (hx[j >> 1] >> 16) : (hx[j >> 1] & 0xFFFF);
+                    const uint32_t sb = (j & 1) ? (sx[j >> 1] >> 16) : (sx[j >> 1] & 0xFFFF);
+                    xs[m][r][j] = ok ? half_bits_to_float(hb) * half_bits_to_float(sb) : 0.0f;
+                    mx[m] = fmaxf(mx[m], fabsf(xs[m][r][j]));
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1)
+                mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], off));
+            if (lane == 0)
+                lds_store_u32(&wmax[2 * wave + m], __float_as_uint(mx[m]));
+        }
+        // (no fence: the weight copies stay in flight)
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        barrier_no_fence();
+        int e[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            float am = wmax[m];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w)
+                am = fmaxf(am, wmax[2 * w + m]);
+            e[m] = code_exponent(am);
+        }
+        // codes of this lane's channels, three signed bytes each, stored per
+        // (limb, token) row of the padded hidden dimension
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int r = 0; r < kRounds; ++r) {
+                const int cl = 8 * lane + 512 * r;
+                if (m < M && cl < kSliceCh) {
+                    uint32_t lw[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int cval = (int)rintf(ldexpf(xs[m][r][j], -e[m]));
+                        const int lo = (int)(int8_t)(cval & 0xFF);
+                        const int c1 = (cval - lo) >> 8;
+                        const int mid = (int)(int8_t)(c1 & 0xFF);
+                        const int hi = (c1 - mid) >> 8;
+                        lw[0][j >> 2] |= (uint32_t)(uint8_t)hi << (8 * (j & 3));
+                        lw[1][j >> 2] |= (uint32_t)(uint8_t)mid << (8 * (j & 3));
+                        lw[2][j >> 2] |= (uint32_t)(uint8_t)lo << (8 * (j & 3));
+                    }
+#pragma unroll
+                    for (int l = 0; l < 3; ++l)
+                        lds_store_u64(reinterpret_cast<unsigned long long *>(codes + (size_t)(l * M + m) * kHPad +
+                                                                             wave * kSliceCh + cl),
+                                      (unsigned long long)lw[l][0] | ((unsigned long long)lw[l][1] << 32));
+                }
+            }
+        // (no fence: the weight copies stay in flight)
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        barrier_no_fence();
+        // A fragment of slot n16 = (limb n16 / 5, token n16 % 5): 16 channels
+        // in the register order of the weight dequantisation (register v, byte
+        // b <- channel 8*(v>>1) + 2*b + (v&1))
+        const int slot_tok = n16 % 5, slot_limb = n16 / 5;
+        const bool slot_live = slot_tok < M && slot_limb < 3;
+        const uint8_t *slot_codes = codes + (size_t)(slot_live ? slot_limb * M + slot_tok : 0) * kHPad;
+#pragma unroll
+        for (int i = 0; i < kUnits; ++i)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ch0 = (wave * kUnits + i) * kUnitH + 32 * grp + 16 * t;
+                const u32x4 d = *reinterpret_cast<const u32x4 *>(slot_codes + ch0);
+                const i32x4 f = {(int32_t)__builtin_amdgcn_perm(d[1], d[0], 0x06040200u),
+                                 (int32_t)__builtin_amdgcn_perm(d[1], d[0], 0x07050301u),
+                                 (int32_t)__builtin_amdgcn_perm(d[3], d[2], 0x06040200u),
+                                 (int32_t)__builtin_amdgcn_perm(d[3], d[2], 0x07050301u)};
+                afr[i][t][0] = slot_live ? f : i32x4{0, 0, 0, 0};
+            }
+        rexp = e[rtok < M ? rtok : 0] - 4;
+    }
 
     // LDS byte offsets of this lane's B fragments (swizzled), per unit
     int boff[kUnits];
@@ -1554,7 +1692,38 @@ template <int kP, int kUnits, bool kLogits, int kTopK, bool kLse>
 Pair make_pair()
 {
     constexpr int kRing = kUnits <= 5 ? 3 : 2;
-    return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits, kTopK, kLse>};
+    return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits, kTopK, kLse, false>};
+}
+
+// One launch, staging inside the verify kernel (up to 2 rows).
+template <int kUnits, bool kLogits>
+Pair make_fused()
+{
+    constexpr int kRing = kUnits <= 5 ? 3 : 2;
+    return Pair{nullptr, verify_kernel<5, kUnits, kRing, kLogits, 0, false, true>};
+}
+
+template <bool kLogits>
+Pair pick_fused(int units)
+{
+    switch (units) {
+    case 1: return make_fused<1, kLogits>();
+    case 2: return make_fused<2, kLogits>();
+    case 3: return make_fused<3, kLogits>();
+    case 4: return make_fused<4, kLogits>();
+    case 5: return make_fused<5, kLogits>();
+    case 6: return make_fused<6, kLogits>();
+    case 7: return make_fused<7, kLogits>();
+    default: return make_fused<8, kLogits>();
+    }
+}
+
+// Whether a greedy call of M rows stages inside the verify kernel: its codes
+// (3 bytes per row and padded channel) must fit the 32 KB partial-sum area.
+bool fused_staging(int M, int units)
+{
+    return M <= 2 && (size_t)M * 3 * units * kWaves * kUnitH + 2 * kWaves * sizeof(float) <=
+                         sizeof(unsigned long long) * 2 * kWaves * kTileRows * kTileRows;
 }
 
 template <int kP, bool kLogits, int kTopK, bool kLse>
@@ -1789,12 +1958,16 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     if (smp && grid > kSampledMaxGrid)
         grid = kSampledMaxGrid;
     int kp = 16;
-    const Pair fn = pick_kernels(a.M, units, lout != nullptr, smp != nullptr, smp ? smp->top_k : 0,
-                                 smp && (smp->top_k == 0 || smp->lse != nullptr), &kp);
-    hipLaunchKernelGGL(fn.stage, dim3(kp), dim3(kStageThreads), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return hip_fail(e, "stage kernel launch");
+    const bool fused = !smp && fused_staging(a.M, units);
+    const Pair fn = fused ? (lout ? pick_fused<true>(units) : pick_fused<false>(units))
+                          : pick_kernels(a.M, units, lout != nullptr, smp != nullptr, smp ? smp->top_k : 0,
+                                         smp && (smp->top_k == 0 || smp->lse != nullptr), &kp);
+    if (fn.stage) {
+        hipLaunchKernelGGL(fn.stage, dim3(kp), dim3(kStageThreads), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return hip_fail(e, "stage kernel launch");
+    }
     const int rs = record_event(ev0, s, "event record before verify kernel");
     if (rs != INT4VH_OK)
         return rs;

@@ -245,6 +245,35 @@ def test_determinism(vh, orc):
         assert np.array_equal(a[k], c[k]), k
 
 
+@pytest.mark.parametrize("H", [32, 96, 1056, 4096, 5120, 8160])
+def test_one_and_two_rows_match_three(vh, orc, H):
+    """Calls of one or two rows stage their activation codes inside the verify
+    kernel; a call of three rows uses the separate staging kernel.  The rows'
+    logits must agree bit for bit, and with the oracle."""
+    V = 3001
+    d = synth.uniform_inputs(3, V, H, seed=H + 11, heavy_frac=0.05)
+    x = d["hidden"].reshape(3, H).copy()
+    x[1, : min(H, 40)] = synth.f16_bits(np.full(min(H, 40), 2.0 ** -24))   # subnormal fp16
+    w = dev(d["packed"])
+    say(f"one/two/three rows H={H}")
+    g3 = run_gpu(vh, x, d["packed"], d["scales"], None, 3, 1, packed_dev=w)
+    for M in (1, 2):
+        o = oracle_case(orc, x[:M], d["packed"], d["scales"], None, M, 1, V, H)
+        g = run_gpu(vh, x[:M], d["packed"], d["scales"], None, M, 1, packed_dev=w)
+        parity.check(g, o, M, 1, None)
+        assert np.array_equal(g["logits"], g3["logits"][:M])
+        assert np.array_equal(g["argmax_ids"], g3["argmax_ids"][:M])
+        gl = run_gpu(vh, x[:M], d["packed"], d["scales"], None, M, 1, logits=False, packed_dev=w)
+        assert np.array_equal(gl["logits_max"], g3["logits_max"][:M])
+        assert np.array_equal(gl["argmax_ids"], g3["argmax_ids"][:M])
+    # a verify block of two positions (one draft) takes the same path
+    drafts = g3["argmax_ids"][:1].astype(np.int32)
+    o = oracle_case(orc, x[:2], d["packed"], d["scales"], drafts, 1, 2, V, H)
+    g = run_gpu(vh, x[:2], d["packed"], d["scales"], drafts, 1, 2, packed_dev=w)
+    parity.check(g, o, 1, 2, drafts)
+    assert g["n_accepted"][0] == 1
+
+
 @pytest.mark.parametrize("R,T", [(4, 4), (2, 8), (16, 1), (3, 5)])
 def test_small_batches(vh, orc, R, T):
     V, H = 5000, 1024
