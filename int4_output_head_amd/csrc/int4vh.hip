@@ -103,10 +103,16 @@ constexpr int kBatchMaxRows = 4096;       // rows per launch of the batch path
 // every call; the rest is written before it is read.
 constexpr size_t kWsTicket = 0;                                   // uint32 ticket
 constexpr size_t kWsKeys = 256;                                   // uint64 [4096] batch winner keys
-constexpr size_t kWsGroupTk = kWsKeys + (size_t)kBatchMaxRows * 8;   // uint32 [64] group tickets
-constexpr size_t kWsDraftSeen = kWsGroupTk + 256;                     // int32 [16] draft logit written
+// Atomics on one 128-byte line serialise at the memory side (about 13 ns
+// each), so a ticket taken by every workgroup at once costs microseconds;
+// the tickets are two-level, one line per group of 16 workgroups.
+constexpr int kGroupWgs = 16;                                     // workgroups per ticket group
+constexpr int kTicketStride = 32;                                 // uint32 per group ticket (128 B)
+constexpr size_t kWsGroupTk = kWsKeys + (size_t)kBatchMaxRows * 8;   // uint32 [64][32] group tickets
+constexpr size_t kWsDraftSeen = kWsGroupTk + (size_t)(kMaxGrid / kGroupWgs) * kTicketStride * 4;
+                                                                  // int32 [16] draft logit written
 constexpr size_t kWsDraftLogit = kWsDraftSeen + 64;                   // float [16] the draft's logit
-constexpr size_t kWsCtlBytes = kWsGroupTk + 512;
+constexpr size_t kWsCtlBytes = kWsDraftSeen + 256;
 constexpr size_t kWsExp = kWsCtlBytes;                            // int32 [4096] step exponents
 constexpr size_t kWsPart = kWsExp + (size_t)kBatchMaxRows * 4;    // uint64 [kMaxGrid][16]
 constexpr size_t kWsFrag = kWsPart + (size_t)kMaxGrid * kMaxRows * 8;   // activation fragments
@@ -181,7 +187,7 @@ struct Args {
     // sampled epilogue (top-k sampling at a temperature; unused when off)
     unsigned long long *part_topk;   // [grid, M, kTopK] per-workgroup top-k keys
     unsigned long long *group_topk;  // [grid / 16, M, kTopK] per-group top-k keys
-    uint32_t *group_ticket;          // [64] per-group tickets, zero between calls
+    uint32_t *group_ticket;          // [64][kTicketStride] per-group tickets (word 0), zero between calls
     int top_k;                // k <= kTopK
     float tau;                // temperature > 0
     const float *dprob;       // [R, T-1] drafter probability of each draft
@@ -972,10 +978,19 @@ verify_kernel(Args a)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if constexpr (kTopK == 0) {
+        // the last workgroup of each group of 16 takes the top-level ticket
         if (threadIdx.x == 0) {
-            const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
-            s_last = (prev == (uint32_t)(G - 1));
+            const int grp = b / kGroupWgs;
+            const int gsz = min(kGroupWgs, G - kGroupWgs * grp);
+            uint32_t *gt = a.group_ticket + (size_t)grp * kTicketStride;
+            bool last = __hip_atomic_fetch_add(gt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                        (uint32_t)(gsz - 1);
+            if (last) {
+                __hip_atomic_store(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)((G + kGroupWgs - 1) / kGroupWgs - 1);
+            }
+            s_last = last;
         }
         __syncthreads();
         if (!s_last)
@@ -989,8 +1004,8 @@ verify_kernel(Args a)
         const int gsz = min(16, G - 16 * grp);
         const int n_grp = (G + 15) / 16;
         if (threadIdx.x == 0) {
-            const uint32_t prev = __hip_atomic_fetch_add(&a.group_ticket[grp], 1u, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t prev = __hip_atomic_fetch_add(&a.group_ticket[(size_t)grp * kTicketStride], 1u,
+                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             s_last = (prev == (uint32_t)(gsz - 1));
         }
         __syncthreads();
@@ -1017,7 +1032,8 @@ verify_kernel(Args a)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __syncthreads();
         if (threadIdx.x == 0) {
-            __hip_atomic_store(&a.group_ticket[grp], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.group_ticket[(size_t)grp * kTicketStride], 0u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
             const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
                                                          __HIP_MEMORY_SCOPE_AGENT);
             s_last = (prev == (uint32_t)(n_grp - 1));
@@ -1258,6 +1274,7 @@ struct RArgs {
     const int32_t *vmap;      // [V] token id of each head row, or null (identity)
     unsigned long long *keys; // [M] per-token winner keys, zero between calls
     uint32_t *ticket;
+    uint32_t *group_ticket;   // [64][kTicketStride] per-group tickets (word 0), zero between calls
     int32_t *exps;            // [n_mt * 128] step exponents
     const u32x4 *frag;        // activation fragments
     u32x4 *frag_out;
@@ -1471,7 +1488,18 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
     // power-of-two step is applied, which gives the same value because the
     // scaled logits stay in the normal range.  Within a lane the column
     // index grows with vb, so a strict > keeps the lowest index on ties.
-    auto finish_item = [&](int it) {
+    // Winners of consecutive items of the same token tile merge here first
+    // (with G a multiple of the number of token tiles, a workgroup keeps one
+    // token tile throughout), so each workgroup takes one atomic per token
+    // and tile change: atomics on one line serialise at the memory side, and
+    // a wave's later loads wait behind its outstanding atomics.
+    unsigned long long run[kRTbPerWave][4];
+#pragma unroll
+    for (int t = 0; t < kRTbPerWave; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            run[t][r] = 0ull;
+    auto finish_item = [&](int it, bool flush) {
         const int vcol = (it / n_mt) * kRVocTile + n16;
 #pragma unroll
         for (int t = 0; t < kRTbPerWave; ++t) {
@@ -1503,9 +1531,14 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
                     bv = take ? ov : bv;
                     bi = take ? oi : bi;
                 }
-                if (n16 == 0 && tok < a.M)
-                    __hip_atomic_fetch_max(&a.keys[tok], order_key(ldexpf(bv, e), bi),
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const unsigned long long key = order_key(ldexpf(bv, e), bi);
+                run[t][r] = key > run[t][r] ? key : run[t][r];
+                if (flush) {
+                    if (n16 == 0 && tok < a.M)
+                        __hip_atomic_fetch_max(&a.keys[tok], run[t][r], __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                    run[t][r] = 0ull;
+                }
             }
         }
     };
@@ -1564,7 +1597,7 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
                     ++kn;
                 }
             }
-            finish_item(b + k * G);
+            finish_item(b + k * G, k == n_my - 1 || (b + (k + 1) * G) % n_mt != (b + k * G) % n_mt);
             zero_acc();
         }
     }
@@ -1575,9 +1608,18 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (tid == 0) {
-        const uint32_t prev = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        lds.last = (prev == (uint32_t)(G - 1));
+        // two levels: the last workgroup of each group of 16 takes the top ticket
+        const int gi = (int)blockIdx.x / kGroupWgs;
+        const int gsz = min(kGroupWgs, G - kGroupWgs * gi);
+        uint32_t *gt = a.group_ticket + (size_t)gi * kTicketStride;
+        bool last = __hip_atomic_fetch_add(gt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                    (uint32_t)(gsz - 1);
+        if (last) {
+            __hip_atomic_store(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                   (uint32_t)((G + kGroupWgs - 1) / kGroupWgs - 1);
+        }
+        lds.last = last;
     }
     __syncthreads();
     if (!lds.last)
@@ -1839,6 +1881,7 @@ int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const 
     a.logits_out = lout;
     a.keys = reinterpret_cast<unsigned long long *>(wsb + kWsKeys);
     a.ticket = reinterpret_cast<uint32_t *>(wsb + kWsTicket);
+    a.group_ticket = reinterpret_cast<uint32_t *>(wsb + kWsGroupTk);
     a.exps = reinterpret_cast<int32_t *>(wsb + kWsExp);
     a.frag = reinterpret_cast<const u32x4 *>(wsb + kWsFrag);
     a.frag_out = reinterpret_cast<u32x4 *>(wsb + kWsFrag);
