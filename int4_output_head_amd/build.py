@@ -1,6 +1,7 @@
 """Build step of the package: compiles the HIP library for gfx950 in-tree."""
 from __future__ import annotations
 
+import ctypes
 import os
 import subprocess
 
@@ -26,6 +27,13 @@ def build_library(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stdout}\n{r.stderr}")
+    # hipcc can finish without an error yet leave a kernel's host stub
+    # undefined; such a library fails at load time, so check that here.
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        os.unlink(tmp)
+        raise RuntimeError(f"built library does not load: {e}") from None
     os.replace(tmp, OUT)
     return OUT
 

@@ -167,6 +167,21 @@ __device__ __forceinline__ void lds_store_u64(unsigned long long *p, unsigned lo
 {
     asm volatile("ds_write_b64 %0, %1" ::"v"(lds_offset(p)), "v"(v) : "memory");
 }
+// One 16-byte-per-lane copy from global memory straight into LDS (lane l
+// lands at lds_dst + 16*l).  Kept out of line of the kernels' bodies.
+template <int kAux>
+__device__ __forceinline__ void copy_to_lds16(const uint8_t *src, uint8_t *lds_dst)
+{
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)lds_dst, 16, 0, kAux);
+}
+
+// A value the compiler cannot prove uniform but the caller knows is (the
+// wave index), moved to a scalar register.
+__device__ __forceinline__ int wave_uniform(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
 __device__ __forceinline__ void lds_store_u32(void *p, uint32_t v)
 {
     asm volatile("ds_write_b32 %0, %1" ::"v"(lds_offset(reinterpret_cast<unsigned long long *>(p))), "v"(v)
@@ -600,7 +615,7 @@ verify_kernel(Args a)
     auto &s_last = mg.last;
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_uniform((int)threadIdx.x >> 6);   // in an SGPR: scalar address math
     const int n16 = lane & 15;   // MFMA row of A / column of B and D
     const int grp = lane >> 4;   // 16-lane group: K sub-block, D rows 4*grp..4*grp+3
     const int G = gridDim.x;
@@ -617,16 +632,32 @@ verify_kernel(Args a)
     // never used: zero activation codes or masked rows), which keeps every
     // wave's number of copies per tile fixed.
     const unsigned long long w_last = a.w_bytes - 16;
+    const unsigned long long tile_bytes = (unsigned long long)kTileRows * (H / 2);
+    const unsigned long long span_bytes = (unsigned long long)a.n_units * 1024;   // bytes a tile's copies touch
+    unsigned int loff[kUnits];                               // lane offsets within a tile, per block
+#pragma unroll
+    for (int m = 0; m < kUnits; ++m) {
+        const int jj = min(wave * kUnits + m, a.n_units - 1);
+        loff[m] = (unsigned int)(jj * 1024 + (lane ^ (jj & 7)) * 16);
+    }
     auto issue_tile = [&](int k) {
         const int tile = b + k * G;
-        const unsigned long long base = (unsigned long long)tile * kTileRows * (H / 2);
+        const unsigned long long base = (unsigned long long)tile * tile_bytes;
         uint8_t *dst = s_ring[k % kRing];
+        if (base + span_bytes <= a.w_bytes) {                // all of the tile's copies inside the head
+            const uint8_t *src = a.w + base;
 #pragma unroll
-        for (int m = 0; m < kUnits; ++m) {
-            const int jj = min(wave * kUnits + m, a.n_units - 1);
-            const unsigned long long off = base + (unsigned long long)jj * 1024 + (unsigned long long)((lane ^ (jj & 7)) * 16);
-            __builtin_amdgcn_global_load_lds(a.w + (off < w_last ? off : w_last),
-                                             (lds_void *)(dst + jj * 1024), 16, 0, INT4VH_WEIGHT_AUX);
+            for (int m = 0; m < kUnits; ++m) {
+                const int jj = min(wave * kUnits + m, a.n_units - 1);
+                copy_to_lds16<INT4VH_WEIGHT_AUX>(src + loff[m], dst + jj * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < kUnits; ++m) {
+                const int jj = min(wave * kUnits + m, a.n_units - 1);
+                const unsigned long long off = base + loff[m];
+                copy_to_lds16<INT4VH_WEIGHT_AUX>(a.w + (off < w_last ? off : w_last), dst + jj * 1024);
+            }
         }
     };
     // ---------------- activation fragments and step exponents
@@ -672,9 +703,8 @@ verify_kernel(Args a)
                 const unsigned long long off = (unsigned long long)(q % kRowBlocks) * 1024 + lane * 16;
                 const uint16_t *src = arr == 0 ? a.scales : a.hidden + (size_t)(arr - 1) * H;
                 // bytes past the row: clamped, masked below
-                __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint8_t *>(src) +
-                                                     (off < row_bytes ? off : row_bytes - 16),
-                                                 (lds_void *)(rows + q * 1024), 16, 0, 0);
+                copy_to_lds16<0>(reinterpret_cast<const uint8_t *>(src) + (off < row_bytes ? off : row_bytes - 16),
+                                 rows + q * 1024);
             }
         }
         // the prologue tiles, unconditional (a tile past the head reads
@@ -794,7 +824,7 @@ verify_kernel(Args a)
         const int row = grp * 4 + r4;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-            const int l = (16 * g + row) / kP;
+            const int l = kP == 16 ? g : (16 * g + row) / kP;   // row < 16: group g is limb g
             shift[g][r4] = l < 3 ? 8 * (2 - l) : -1;
         }
     }
