@@ -817,15 +817,16 @@ verify_kernel(Args a)
         const int jj = gc >> 6;
         boff[i] = (jj * 64 + ((gc & 63) ^ (jj & 7))) * 16;
     }
-    // limb weight (shift) of each group's D rows this lane receives
-    int shift[kGroups][4];
+    // limb weight (2^16, 2^8, 1; 0 for rows past the three limbs) of each
+    // group's D rows this lane receives
+    double limb_w[kGroups][4];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
         const int row = grp * 4 + r4;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
             const int l = kP == 16 ? g : (16 * g + row) / kP;   // row < 16: group g is limb g
-            shift[g][r4] = l < 3 ? 8 * (2 - l) : -1;
+            limb_w[g][r4] = l < 3 ? (double)(1 << (8 * (2 - l))) : 0.0;
         }
     }
 
@@ -847,16 +848,16 @@ verify_kernel(Args a)
     const int rt = rlane ? rtok : 0;
     auto reduce_tile = [&](int k) {
         const int buf = k & 1;
-        long long code = 0;
+        double code = 0.0;                 // integer-valued, |code| < 2^47: exact
 #pragma unroll
         for (int j = 0; j < kRowsPerTok; ++j)
 #pragma unroll
             for (int w = 0; w < kWaves; ++w)
-                code += (long long)s_part[buf][w][rt + kP * j][n16];
+                code += __longlong_as_double((long long)s_part[buf][w][rt + kP * j][n16]);
         unsigned long long key = 0ull;
         if (rlane) {
             const int v = (b + k * G) * kTileRows + n16;
-            const float val = (float)ldexp((double)code, rexp);   // the one rounding
+            const float val = (float)ldexp(code, rexp);   // the one rounding
             if (v < V) {
                 if (better(val, v, bv, bi)) {
                     bv = val;
@@ -950,16 +951,17 @@ verify_kernel(Args a)
         if (k > 0)
             reduce_tile(k - 1);
 
-        // this wave's partial codes, limbs combined (exact int64), one per D row
+        // this wave's partial codes, limbs combined, one per D row: binary64
+        // holds them exactly (|value| < 2^44), and the combination is three
+        // conversions and two fused multiply-adds instead of 64-bit shifts
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-            long long val = 0;
+            double val = (double)acc[0][r4] * limb_w[0][r4];
 #pragma unroll
-            for (int g = 0; g < kGroups; ++g)
-                if (shift[g][r4] >= 0)
-                    val += (long long)acc[g][r4] << shift[g][r4];
+            for (int g = 1; g < kGroups; ++g)
+                val = __builtin_fma((double)acc[g][r4], limb_w[g][r4], val);
             // rows of tokens >= M hold zero activation codes, so val is 0
-            lds_store_u64(&s_part[k & 1][wave][grp * 4 + r4][n16], (unsigned long long)val);
+            lds_store_u64(&s_part[k & 1][wave][grp * 4 + r4][n16], (unsigned long long)__double_as_longlong(val));
         }
     }
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
