@@ -386,6 +386,25 @@ __device__ __forceinline__ uint64_t lse_pack(float m, float s)
     return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)__float_as_uint(m);
 }
 
+// (m, s) pairs [n <= 16] of one row, stored [n][M] from `pairs`: lane j of
+// each 16-lane group loads pair j of row `row` (all loads in flight at once)
+// and a fixed butterfly over the 16 lanes combines them; every lane of the
+// group ends with the same pair.  Called by all lanes of the wave.
+__device__ __forceinline__ void lse_gather16(const uint64_t *pairs, int n, int M, int row, float &m, float &s)
+{
+    const int j = threadIdx.x & 15;
+    const uint64_t pr = __hip_atomic_load(&pairs[(size_t)(j < n ? j : 0) * M + row], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    m = j < n ? __uint_as_float((uint32_t)pr) : -__builtin_huge_valf();
+    s = j < n ? __uint_as_float((uint32_t)(pr >> 32)) : 0.0f;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+        const float mo = __shfl_xor(m, off);
+        const float so = __shfl_xor(s, off);
+        lse_combine(m, s, mo, so);
+    }
+}
+
 // Merge up to 16 published top-k lists ([n_lists][M][kTopK] keys, rank
 // order) per token; a workgroup of 512 threads, wave w handling tokens 2w
 // and 2w+1 with 32 lanes each.  Each half of the 32 lanes folds the lists of
@@ -400,21 +419,26 @@ __device__ __forceinline__ unsigned long long merge_topk_lists(const unsigned lo
     const int mm = m < M ? m : M - 1;
     const int h = (lane >> 4) & 1;
     const int j = lane & 15;
+    // lists 2i + h, even i by rank and odd i reversed; every load issued
+    // before any is used (clamped to a valid slot, zero = empty when absent)
     unsigned long long e[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int w = 2 * i + h;
-        const int r = i == 0 ? j : 15 - j;       // the first list by rank, the others reversed
-        e[i] = (w < n_lists && r < kTopK)
-                   ? __hip_atomic_load(&lists[((size_t)w * M + mm) * kTopK + r], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)
-                   : 0ull;
+        const int r = (i & 1) == 0 ? j : 15 - j;
+        const bool live = w < n_lists && r < kTopK;
+        const unsigned long long v = __hip_atomic_load(&lists[((size_t)(live ? w : 0) * M + mm) * kTopK + (live ? r : 0)],
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        e[i] = live ? v : 0ull;
     }
-    unsigned long long c = e[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i)
-        if (2 * i < n_lists)
-            c = dlist_merge(c, e[i], lane);
+    // a merge tree (empty lists merge harmlessly): depth 3 instead of 7
+    const unsigned long long c0 = dlist_merge(e[0], e[1], lane);
+    const unsigned long long c1 = dlist_merge(e[2], e[3], lane);
+    const unsigned long long c2 = dlist_merge(e[4], e[5], lane);
+    const unsigned long long c3 = dlist_merge(e[6], e[7], lane);
+    const unsigned long long d0 = dlist_merge(c0, key_dpp<0x140>(c1), lane);   // row_mirror: reversed
+    const unsigned long long d1 = dlist_merge(c2, key_dpp<0x140>(c3), lane);
+    const unsigned long long c = dlist_merge(d0, key_dpp<0x140>(d1), lane);
     return dlist_merge(c, key_shfl(c, ((lane ^ 16) & ~15) | (15 - j)), lane);
 }
 
@@ -1050,15 +1074,14 @@ verify_kernel(Args a)
             if (m < M && ((lane >> 4) & 1) == 0 && n16 < kTopK)
                 __hip_atomic_store(&a.group_topk[((size_t)grp * M + m) * kTopK + n16], mine,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (kLse && m < M && (lane & 31) == 0) {
-                float gm = -__builtin_huge_valf(), gs = 0.0f;
-                for (int w = 0; w < gsz; ++w) {
-                    const uint64_t pr = __hip_atomic_load(&a.part_lse[(size_t)(16 * grp + w) * M + m],
-                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    lse_combine(gm, gs, __uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32)));
-                }
-                __hip_atomic_store(&a.group_lse[(size_t)grp * M + m], lse_pack(gm, gs), __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+            if constexpr (kLse) {
+                // lane n16 of the token's 16-lane group loads workgroup n16's
+                // pair; a fixed butterfly combines the 16
+                float gm, gs;
+                lse_gather16(a.part_lse + (size_t)16 * grp * M, gsz, M, m < M ? m : 0, gm, gs);
+                if (m < M && (lane & 31) == 0)
+                    __hip_atomic_store(&a.group_lse[(size_t)grp * M + m], lse_pack(gm, gs), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -1191,20 +1214,17 @@ verify_kernel(Args a)
             a.topk_ids[m * a.top_k + slot] = hi;
             a.topk_logits[m * a.top_k + slot] = hv;
         }
+        // log sum exp(logit / tau) over the whole vocabulary, from the
+        // group pairs (lane-parallel loads, fixed butterfly)
+        float lse = 0.0f;
+        if constexpr (kLse) {
+            float gm, gs;
+            lse_gather16(a.group_lse, n_grp, M, mm, gm, gs);
+            lse = (gm + __log2f(gs)) * 0.6931471805599453f;
+        }
         if (slot == 0 && m < M) {
-            // log sum exp(logit / tau) over the whole vocabulary
-            float lse = 0.0f;
-            if constexpr (kLse) {
-                float gm = -__builtin_huge_valf(), gs = 0.0f;
-                for (int w = 0; w < n_grp; ++w) {
-                    const uint64_t pr = __hip_atomic_load(&a.group_lse[(size_t)w * M + m], __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT);
-                    lse_combine(gm, gs, __uint_as_float((uint32_t)pr), __uint_as_float((uint32_t)(pr >> 32)));
-                }
-                lse = (gm + __log2f(gs)) * 0.6931471805599453f;
-                if (a.lse_out)
-                    a.lse_out[m] = lse;
-            }
+            if (kLse && a.lse_out)
+                a.lse_out[m] = lse;
             int ok = 0;
             if (drafted) {
                 const int di = req * (T - 1) + t;
