@@ -1028,7 +1028,7 @@ verify_kernel(Args a)
     // wave waits until its store is acknowledged before the barrier, so every
     // store has landed before the ticket is incremented, and the last
     // workgroup reads them with agent-scope atomic loads.
-    if (rlane && n16 == 0)
+    if (kTopK == 0 && rlane && n16 == 0)           // (the sampled epilogue's winners are in its lists)
         __hip_atomic_store(&a.part[(size_t)b * M + rtok], pack_pair(bv, bi), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -1102,59 +1102,62 @@ verify_kernel(Args a)
     // One memory round trip: every load below is issued before any is used.
     // Thread (slot, m) takes the winners of workgroups slot, slot+32, ... for
     // token m (agent-scope loads: the lines may be stale in this XCD's L2);
-    // the threads below R*(T-1) also fetch one draft id each.
+    // the threads below R*(T-1) also fetch one draft id each.  (The sampled
+    // epilogue takes its winners from the merged top-k lists instead.)
     {
         const int m = threadIdx.x & 15;
         const int slot = threadIdx.x >> 4;   // 0..31
         const int mm = m < M ? m : M - 1;    // rows past M repeat a real one (never written out)
         const int n_draft = a.R * (a.T - 1);
         const int dft = (int)threadIdx.x < n_draft ? a.draft[threadIdx.x] : 0;
-        float v0 = -__builtin_huge_valf();
-        int i0 = 0x7FFFFFFF;
-        constexpr int kPerThread = kMaxGrid / 32;
-        constexpr int kBatch = 8;
+        if constexpr (kTopK == 0) {
+            float v0 = -__builtin_huge_valf();
+            int i0 = 0x7FFFFFFF;
+            constexpr int kPerThread = kMaxGrid / 32;
+            constexpr int kBatch = 8;
 #pragma unroll
-        for (int j0 = 0; j0 < kPerThread; j0 += kBatch) {
-            if (32 * j0 >= G)
-                break;
-            uint64_t p[kBatch];
+            for (int j0 = 0; j0 < kPerThread; j0 += kBatch) {
+                if (32 * j0 >= G)
+                    break;
+                uint64_t p[kBatch];
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                int bb = slot + 32 * (j0 + j);
-                bb = bb < G ? bb : G - 1;    // repeats are harmless for a maximum
-                p[j] = __hip_atomic_load(&a.part[(size_t)bb * M + mm], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-            }
+                for (int j = 0; j < kBatch; ++j) {
+                    int bb = slot + 32 * (j0 + j);
+                    bb = bb < G ? bb : G - 1;    // repeats are harmless for a maximum
+                    p[j] = __hip_atomic_load(&a.part[(size_t)bb * M + mm], __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+                }
 #pragma unroll
-            for (int j = 0; j < kBatch; ++j) {
-                const float pv = __uint_as_float((uint32_t)p[j]);
-                const int pi = (int)(uint32_t)(p[j] >> 32);
-                if (better(pv, pi, v0, i0)) {
-                    v0 = pv;
-                    i0 = pi;
+                for (int j = 0; j < kBatch; ++j) {
+                    const float pv = __uint_as_float((uint32_t)p[j]);
+                    const int pi = (int)(uint32_t)(p[j] >> 32);
+                    if (better(pv, pi, v0, i0)) {
+                        v0 = pv;
+                        i0 = pi;
+                    }
                 }
             }
-        }
-        // the four slots of this wave (lanes m, m+16, m+32, m+48)
+            // the four slots of this wave (lanes m, m+16, m+32, m+48)
 #pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-            const float ov = __shfl_xor(v0, off);
-            const int oi = __shfl_xor(i0, off);
-            if (better(ov, oi, v0, i0)) {
-                v0 = ov;
-                i0 = oi;
+            for (int off = 16; off <= 32; off <<= 1) {
+                const float ov = __shfl_xor(v0, off);
+                const int oi = __shfl_xor(i0, off);
+                if (better(ov, oi, v0, i0)) {
+                    v0 = ov;
+                    i0 = oi;
+                }
             }
-        }
-        const int wv = threadIdx.x >> 6;
-        if ((threadIdx.x & 63) < 16) {
-            s_fv[wv][m] = v0;
-            s_fi[wv][m] = i0;
+            const int wv = threadIdx.x >> 6;
+            if ((threadIdx.x & 63) < 16) {
+                s_fv[wv][m] = v0;
+                s_fi[wv][m] = i0;
+            }
         }
         if ((int)threadIdx.x < n_draft)
             s_draft[threadIdx.x] = dft;
     }
     __syncthreads();
-    if (threadIdx.x < (unsigned)M) {
+    if (kTopK == 0 && threadIdx.x < (unsigned)M) {
         const int m = threadIdx.x;
         float fv[kWaves];
         int fi[kWaves];
@@ -1202,6 +1205,10 @@ verify_kernel(Args a)
         const int d = drafted ? s_draft[req * (T - 1) + t] : -1;
         const float hv = key_value(mine);
         const int hi = key_index(mine);
+        if (slot == 0 && m < M) {                     // rank 0: the greedy winner
+            a.logits_max[m] = hv;
+            a.argmax[m] = a.vmap ? a.vmap[hi] : hi;
+        }
         const float lmax = key_value(key_shfl(mine, lane & ~15));
         const float e = n16 < a.top_k ? expf((hv - lmax) / a.tau) : 0.0f;
         float sum = e, e_d = (n16 < a.top_k && hi == d) ? e : 0.0f;
