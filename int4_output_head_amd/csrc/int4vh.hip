@@ -182,6 +182,36 @@ __device__ __forceinline__ int wave_uniform(int v)
     return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Cross-lane moves within a 16-lane DPP row (no LDS traffic, unlike
+// __shfl): row_ror:n gives each lane the value of the lane n places before
+// it in its row, cyclically.
+template <int kCtl>
+__device__ __forceinline__ float dpp_f32(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtl, 0xF, 0xF, false));
+}
+template <int kCtl>
+__device__ __forceinline__ int dpp_i32(int x)
+{
+    return __builtin_amdgcn_update_dpp(0, x, kCtl, 0xF, 0xF, false);
+}
+constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
+
+// Maximum of x over the wave, in every lane (rotations within the rows,
+// then the four row results).  Called by all lanes.
+__device__ __forceinline__ float wave_max(float x)
+{
+    x = fmaxf(x, dpp_f32<kRowRor1>(x));
+    x = fmaxf(x, dpp_f32<kRowRor2>(x));
+    x = fmaxf(x, dpp_f32<kRowRor4>(x));
+    x = fmaxf(x, dpp_f32<kRowRor8>(x));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ __forceinline__ void lds_store_u32(void *p, uint32_t v)
 {
     asm volatile("ds_write_b32 %0, %1" ::"v"(lds_offset(reinterpret_cast<unsigned long long *>(p))), "v"(v)
@@ -235,6 +265,44 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t b)
 __device__ __forceinline__ bool better(float v1, int i1, float v2, int i2)
 {
     return v1 > v2 || (v1 == v2 && i1 < i2);
+}
+
+// The better (value, index) pair over the lane's 16-lane row, in every lane
+// of the row (rotations: each step doubles the window a lane has seen).
+__device__ __forceinline__ void row_best16(float &v, int &i)
+{
+#define INT4VH_ROW_BEST_STEP(C)                                        \
+    {                                                                  \
+        const float ov = dpp_f32<C>(v);                                \
+        const int oi = dpp_i32<C>(i);                                  \
+        const bool take = better(ov, oi, v, i);                        \
+        v = take ? ov : v;                                             \
+        i = take ? oi : i;                                             \
+    }
+    INT4VH_ROW_BEST_STEP(kRowRor1)
+    INT4VH_ROW_BEST_STEP(kRowRor2)
+    INT4VH_ROW_BEST_STEP(kRowRor4)
+    INT4VH_ROW_BEST_STEP(kRowRor8)
+#undef INT4VH_ROW_BEST_STEP
+}
+
+// (max, sum) pairs of exp2 terms and plain sums over the lane's 16-lane row,
+// in every lane of the row.
+__device__ __forceinline__ void lse_combine(float &m, float &s, float mo, float so);
+__device__ __forceinline__ void row_lse16(float &m, float &s)
+{
+    lse_combine(m, s, dpp_f32<kRowRor1>(m), dpp_f32<kRowRor1>(s));
+    lse_combine(m, s, dpp_f32<kRowRor2>(m), dpp_f32<kRowRor2>(s));
+    lse_combine(m, s, dpp_f32<kRowRor4>(m), dpp_f32<kRowRor4>(s));
+    lse_combine(m, s, dpp_f32<kRowRor8>(m), dpp_f32<kRowRor8>(s));
+}
+__device__ __forceinline__ float row_sum16(float x)
+{
+    x += dpp_f32<kRowRor1>(x);
+    x += dpp_f32<kRowRor2>(x);
+    x += dpp_f32<kRowRor4>(x);
+    x += dpp_f32<kRowRor8>(x);
+    return x;
 }
 
 __device__ __forceinline__ uint64_t pack_pair(float v, int i)
@@ -388,7 +456,7 @@ __device__ __forceinline__ uint64_t lse_pack(float m, float s)
 
 // (m, s) pairs [n <= 16] of one row, stored [n][M] from `pairs`: lane j of
 // each 16-lane group loads pair j of row `row` (all loads in flight at once)
-// and a fixed butterfly over the 16 lanes combines them; every lane of the
+// and a fixed sequence of row rotations combines them; every lane of the
 // group ends with the same pair.  Called by all lanes of the wave.
 __device__ __forceinline__ void lse_gather16(const uint64_t *pairs, int n, int M, int row, float &m, float &s)
 {
@@ -397,12 +465,7 @@ __device__ __forceinline__ void lse_gather16(const uint64_t *pairs, int n, int M
                                           __HIP_MEMORY_SCOPE_AGENT);
     m = j < n ? __uint_as_float((uint32_t)pr) : -__builtin_huge_valf();
     s = j < n ? __uint_as_float((uint32_t)(pr >> 32)) : 0.0f;
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-        const float mo = __shfl_xor(m, off);
-        const float so = __shfl_xor(s, off);
-        lse_combine(m, s, mo, so);
-    }
+    row_lse16(m, s);
 }
 
 // Merge up to 16 published top-k lists ([n_lists][M][kTopK] keys, rank
@@ -562,9 +625,7 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
         for (int j = 0; j < 16; ++j)
             am = fmaxf(am, fabsf(xs[it][j]));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1)
-        am = fmaxf(am, __shfl_xor(am, off));
+    am = wave_max(am);
     if ((threadIdx.x & 63) == 0)
         s_red[threadIdx.x >> 6] = am;
     __syncthreads();
@@ -764,9 +825,7 @@ verify_kernel(Args a)
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1)
-                mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], off));
+            mx[m] = wave_max(mx[m]);
             if (lane == 0)
                 lds_store_u32(&wmax[2 * wave + m], __float_as_uint(mx[m]));
         }
@@ -993,29 +1052,16 @@ verify_kernel(Args a)
     reduce_tile(n_my - 1);
 
     // ---------------- per-workgroup best per token
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
+    row_best16(bv, bi);
     if constexpr (kTopK > 0) {
         // lane n16 = j publishes the rank-j key of the workgroup's list;
-        // the 16 lanes' (max, sum) pairs combine (fixed butterfly) and lane
+        // the 16 lanes' (max, sum) pairs combine (fixed rotations) and lane
         // 0 of the token publishes them
         if (rlane && n16 < kTopK)
             __hip_atomic_store(&a.part_topk[((size_t)b * M + rtok) * kTopK + n16], dl,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if constexpr (kLse) {
-#pragma unroll
-            for (int off = 8; off >= 1; off >>= 1) {
-                const float mo = __shfl_xor(lm, off);
-                const float so = __shfl_xor(ls, off);
-                lse_combine(lm, ls, mo, so);
-            }
+            row_lse16(lm, ls);
             if (rlane && n16 == 0)
                 __hip_atomic_store(&a.part_lse[(size_t)b * M + rtok], lse_pack(lm, ls), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -1076,7 +1122,7 @@ verify_kernel(Args a)
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if constexpr (kLse) {
                 // lane n16 of the token's 16-lane group loads workgroup n16's
-                // pair; a fixed butterfly combines the 16
+                // pair; fixed row rotations combine the 16
                 float gm, gs;
                 lse_gather16(a.part_lse + (size_t)16 * grp * M, gsz, M, m < M ? m : 0, gm, gs);
                 if (m < M && (lane & 31) == 0)
@@ -1193,7 +1239,7 @@ verify_kernel(Args a)
         // Sampled epilogue, final merge over the group lists, then the
         // token's target probability of its draft from the k logits (top-k
         // sampling at temperature tau): lane j of the token's first 16-lane
-        // group holds rank j; sums are fixed butterflies over the 16 lanes.
+        // group holds rank j; sums are fixed rotations over the 16 lanes.
         const int n_grp = (G + 15) / 16;
         const unsigned long long mine = merge_topk_lists<kTopK>(a.group_topk, n_grp, M, lane);
         const int m = 2 * wave + (lane >> 5);
@@ -1212,17 +1258,14 @@ verify_kernel(Args a)
         const float lmax = key_value(key_shfl(mine, lane & ~15));
         const float e = n16 < a.top_k ? expf((hv - lmax) / a.tau) : 0.0f;
         float sum = e, e_d = (n16 < a.top_k && hi == d) ? e : 0.0f;
-#pragma unroll
-        for (int off = 8; off >= 1; off >>= 1) {
-            sum += __shfl_xor(sum, off);
-            e_d += __shfl_xor(e_d, off);
-        }
+        sum = row_sum16(sum);
+        e_d = row_sum16(e_d);
         if (slot < a.top_k && m < M) {
             a.topk_ids[m * a.top_k + slot] = hi;
             a.topk_logits[m * a.top_k + slot] = hv;
         }
         // log sum exp(logit / tau) over the whole vocabulary, from the
-        // group pairs (lane-parallel loads, fixed butterfly)
+        // group pairs (lane-parallel loads, fixed row rotations)
         float lse = 0.0f;
         if constexpr (kLse) {
             float gm, gs;
@@ -1390,9 +1433,7 @@ __global__ void __launch_bounds__(kRStageThreads) stage_rows_kernel(RArgs a)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 am = fmaxf(am, fabsf(xs[j][i]));
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1)
-            am = fmaxf(am, __shfl_xor(am, off));
+        am = wave_max(am);
         if ((tid & 63) == 0)
             s_am[n][sub / 64] = am;
         __syncthreads();
@@ -1582,14 +1623,7 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
                     if (kLogits && tok < a.M && v < a.V)
                         a.logits_out[(size_t)tok * a.V + v] = ldexpf(u, e);
                 }
-#pragma unroll
-                for (int off = 8; off >= 1; off >>= 1) {
-                    const float ov = __shfl_xor(bv, off);
-                    const int oi = __shfl_xor(bi, off);
-                    const bool take = ov > bv || (ov == bv && oi < bi);
-                    bv = take ? ov : bv;
-                    bi = take ? oi : bi;
-                }
+                row_best16(bv, bi);
                 const unsigned long long key = order_key(ldexpf(bv, e), bi);
                 run[t][r] = key > run[t][r] ? key : run[t][r];
                 if (flush) {
