@@ -212,6 +212,24 @@ __device__ __forceinline__ float wave_max(float x)
     return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Three 8-byte LDS reads, complete on return.  Written as one asm block:
+// reads of a ring slot that the weight copies also fill would otherwise
+// make the compiler wait for every copy in flight (it cannot tell the
+// slots apart).
+__device__ __forceinline__ void lds_load3_u64(const void *p0, const void *p1, const void *p2, uint2 &v0, uint2 &v1,
+                                              uint2 &v2)
+{
+    asm volatile("ds_read_b64 %0, %3\n\t"
+                 "ds_read_b64 %1, %4\n\t"
+                 "ds_read_b64 %2, %5\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(v0), "=&v"(v1), "=&v"(v2)
+                 : "v"(lds_offset(reinterpret_cast<unsigned long long *>(const_cast<void *>(p0)))),
+                   "v"(lds_offset(reinterpret_cast<unsigned long long *>(const_cast<void *>(p1)))),
+                   "v"(lds_offset(reinterpret_cast<unsigned long long *>(const_cast<void *>(p2))))
+                 : "memory");
+}
+
 __device__ __forceinline__ void lds_store_u32(void *p, uint32_t v)
 {
     asm volatile("ds_write_b32 %0, %1" ::"v"(lds_offset(reinterpret_cast<unsigned long long *>(p))), "v"(v)
@@ -776,7 +794,6 @@ verify_kernel(Args a)
         constexpr int kSliceCh = kUnits * kUnitH;           // channels of a wave's slice
         constexpr int kHPad = kWaves * kSliceCh;              // padded hidden dimension
         constexpr int kRowBlocks = kHPad * 2 / 1024;          // 1 KB blocks of one padded fp16 row
-        constexpr int kRounds = (kSliceCh + 511) / 512;       // 8-channel chunks per lane
         static_assert(3 * kHPad * 2 <= kTileBytes, "scale and hidden rows fit one ring slot");
         uint8_t *rows = s_ring[kRing - 1];                    // [scales | hidden 0 | hidden 1], kHPad each
         uint8_t *codes = reinterpret_cast<uint8_t *>(&s_part[0][0][0][0]);     // [3][M][kHPad]
@@ -801,23 +818,29 @@ verify_kernel(Args a)
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((kRing - 1) * kUnits));
         barrier_no_fence();
 
-        float xs[2][kRounds][8];
+        // Thread t takes the 4-channel chunks t, t + 512, ... of the padded
+        // row (an even share per SIMD); channels past H give zero codes.
+        constexpr int kChunks4 = kHPad / 4;
+        constexpr int kR4 = (kChunks4 + kThreads - 1) / kThreads;
+        float xs[2][kR4][4];
         float mx[2] = {0.0f, 0.0f};
 #pragma unroll
-        for (int r = 0; r < kRounds; ++r) {
-            const int cl = 8 * lane + 512 * r;                  // channel within the slice
-            const int c0 = wave * kSliceCh + cl;
-            const bool in_slice = cl < kSliceCh;
-            const u32x4 sx = *reinterpret_cast<const u32x4 *>(rows + 2 * (in_slice ? c0 : 0));
+        for (int r = 0; r < kR4; ++r) {
+            const int c = (int)threadIdx.x + kThreads * r;
+            const bool in_pad = c < kChunks4;
+            const int ch = in_pad ? 4 * c : 0;
+            uint2 sx, hxm[2];
+            lds_load3_u64(rows + 2 * ch, rows + 2 * (kHPad + ch), rows + 2 * ((M > 1 ? 2 : 1) * kHPad + ch), sx,
+                          hxm[0], hxm[1]);
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const bool ok = m < M && in_slice && c0 < H;
-                const u32x4 hx = *reinterpret_cast<const u32x4 *>(rows + 2 * ((1 + (m < M ? m : 0)) * kHPad +
-                                                                                (in_slice ? c0 : 0)));
+                const bool ok = m < M && in_pad && 4 * c < H;
+                const uint2 hx = hxm[m];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const uint32_t hb = (j & 1) ? (hx[j >> 1] >> 16) : (hx[j >> 1] & 0xFFFF);
-                    const uint32_t sb = (j & 1) ? (sx[j >> 1] >> 16) : (sx[j >> 1] & 0xFFFF);
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t hw = j < 2 ? hx.x : hx.y, sw = j < 2 ? sx.x : sx.y;
+                    const uint32_t hb = (j & 1) ? (hw >> 16) : (hw & 0xFFFF);
+                    const uint32_t sb = (j & 1) ? (sw >> 16) : (sw & 0xFFFF);
                     xs[m][r][j] = ok ? half_bits_to_float(hb) * half_bits_to_float(sb) : 0.0f;
                     mx[m] = fmaxf(mx[m], fabsf(xs[m][r][j]));
                 }
@@ -841,31 +864,31 @@ verify_kernel(Args a)
                 am = fmaxf(am, wmax[2 * w + m]);
             e[m] = code_exponent(am);
         }
-        // codes of this lane's channels, three signed bytes each, stored per
-        // (limb, token) row of the padded hidden dimension
+        // Codes, as three signed bytes each, stored per (limb, token) row of
+        // the padded hidden dimension.  |code| <= kCodeMax = 0x7F7F7F, so
+        // code + 0x808080 lies in [0, 2^24) and its bytes are the limbs
+        // (low first) offset by 128: byte i of the biased value, xor 0x80, is
+        // the signed limb of weight 2^(8i) -- the same split as stage_kernel.
+        // Four codes' bytes of one limb are gathered with byte permutes.
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int r = 0; r < kRounds; ++r) {
-                const int cl = 8 * lane + 512 * r;
-                if (m < M && cl < kSliceCh) {
-                    uint32_t lw[3][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}};
+            for (int r = 0; r < kR4; ++r) {
+                const int c = (int)threadIdx.x + kThreads * r;
+                if (m < M && c < kChunks4) {
+                    uint32_t u[4];
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        const int cval = (int)rintf(ldexpf(xs[m][r][j], -e[m]));
-                        const int lo = (int)(int8_t)(cval & 0xFF);
-                        const int c1 = (cval - lo) >> 8;
-                        const int mid = (int)(int8_t)(c1 & 0xFF);
-                        const int hi = (c1 - mid) >> 8;
-                        lw[0][j >> 2] |= (uint32_t)(uint8_t)hi << (8 * (j & 3));
-                        lw[1][j >> 2] |= (uint32_t)(uint8_t)mid << (8 * (j & 3));
-                        lw[2][j >> 2] |= (uint32_t)(uint8_t)lo << (8 * (j & 3));
+                    for (int j = 0; j < 4; ++j)
+                        u[j] = (uint32_t)((int)rintf(ldexpf(xs[m][r][j], -e[m])) + 0x808080);
+#pragma unroll
+                    for (int l = 0; l < 3; ++l) {            // limb l: 0 = high (byte 2) ... 2 = low (byte 0)
+                        const uint32_t bi = 2 - l;
+                        const uint32_t sel = ((4 + bi) << 8) | bi;
+                        const uint32_t p01 = __builtin_amdgcn_perm(u[1], u[0], sel);
+                        const uint32_t p23 = __builtin_amdgcn_perm(u[3], u[2], sel);
+                        lds_store_u32(codes + (size_t)(l * M + m) * kHPad + 4 * c,
+                                      __builtin_amdgcn_perm(p23, p01, 0x05040100u) ^ 0x80808080u);
                     }
-#pragma unroll
-                    for (int l = 0; l < 3; ++l)
-                        lds_store_u64(reinterpret_cast<unsigned long long *>(codes + (size_t)(l * M + m) * kHPad +
-                                                                             wave * kSliceCh + cl),
-                                      (unsigned long long)lw[l][0] | ((unsigned long long)lw[l][1] << 32));
                 }
             }
         // (no fence: the weight copies stay in flight)
