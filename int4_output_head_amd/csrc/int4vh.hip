@@ -700,9 +700,15 @@ verify_kernel(Args a)
         int accept[kMaxRows];
         int last;
     };
+    // Sampled epilogue: a per-token buffer of candidate keys, sorted into the
+    // top-k list 16 at a time -- where the LDS budget leaves room for it
+    // (otherwise candidates are inserted into the list directly).
+    constexpr bool kCBuf = kTopK > 0 && (size_t)kRing * kTileBytes + 2 * kWaves * kTileRows * kTileRows * 8 +
+                                                (size_t)kWaves * 2 * 16 * 8 <= 160 * 1024;
     struct Lds {
         uint8_t ring[kRing][kTileBytes];
         unsigned long long part[2][kWaves][kTileRows][kTileRows];
+        unsigned long long cbuf[kCBuf ? kWaves : 0][2][16];   // [wave][token 2w / 2w+1][slot]
     };
     static_assert(sizeof(Merge) <= sizeof(uint8_t[kRing][kTileBytes]), "merge area");
     static_assert(sizeof(Lds) <= 160 * 1024, "LDS budget");
@@ -944,6 +950,18 @@ verify_kernel(Args a)
     unsigned long long dl = 0ull;
     float lm = -__builtin_huge_valf(), ls = 0.0f;
     const float zscale = 1.4426950408889634f / a.tau;
+    int cnt0 = 0, cnt1 = 0;             // buffered candidates of the wave's two tokens (wave-uniform)
+    // sort the buffered candidates of both tokens into their lists (all lanes)
+    auto flush_cand = [&]() {
+        if constexpr (kCBuf) {
+            const int cnt = lane < 16 ? cnt0 : cnt1;
+            const unsigned long long v = (lane < 32 && n16 < cnt) ? lds.cbuf[wave][(lane >> 4) & 1][n16] : 0ull;
+            const unsigned long long srt = row_sort16(v, n16);
+            dl = dlist_merge(dl, key_dpp<0x140>(srt), lane);      // row_mirror: rank 15-j
+            cnt0 = 0;
+            cnt1 = 0;
+        }
+    };
     int my_draft = -1;
     if (kTopK > 0 && rlane && a.T > 1 && (rtok % a.T) < a.T - 1)
         my_draft = a.draft[(rtok / a.T) * (a.T - 1) + rtok % a.T];
@@ -982,7 +1000,26 @@ verify_kernel(Args a)
                     a.logits_out[(size_t)rtok * V + v] = val;
             }
         }
-        if constexpr (kTopK > 0) {
+        if constexpr (kCBuf) {
+            // the tile's keys that beat the list's last kept rank go to the
+            // token's candidate buffer; a full buffer is sorted and merged
+            // into the list first (wave-uniform control flow)
+            const unsigned long long th0 = key_readlane(dl, kTopK - 1);
+            const unsigned long long th1 = key_readlane(dl, 16 + kTopK - 1);
+            const bool is_cand = key > (lane < 16 ? th0 : th1);
+            const unsigned long long cand = __ballot(is_cand);
+            const uint32_t m0 = (uint32_t)cand & 0xFFFFu, m1 = (uint32_t)(cand >> 16) & 0xFFFFu;
+            const int n0 = __builtin_popcount(m0), n1 = __builtin_popcount(m1);
+            if (cnt0 + n0 > 16 || cnt1 + n1 > 16)
+                flush_cand();
+            if (is_cand) {
+                const uint32_t mrow = lane < 16 ? m0 : m1;
+                const int slot = (lane < 16 ? cnt0 : cnt1) + __builtin_popcount(mrow & ((1u << n16) - 1u));
+                lds.cbuf[wave][(lane >> 4) & 1][slot] = key;
+            }
+            cnt0 += n0;
+            cnt1 += n1;
+        } else if constexpr (kTopK > 0) {
             // insert the tile's keys that beat the list's last kept rank: a
             // sort and one merge when a group has more than two, else one per
             // group and iteration (wave-uniform control flow, all lanes active)
@@ -1073,6 +1110,8 @@ verify_kernel(Args a)
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier_no_fence();
     reduce_tile(n_my - 1);
+    if (cnt0 + cnt1 > 0)
+        flush_cand();
 
     // ---------------- per-workgroup best per token
     row_best16(bv, bi);
