@@ -983,9 +983,11 @@ verify_kernel(Args a)
             const int v = (b + k * G) * kTileRows + n16;
             const float val = (float)ldexp(code, rexp);   // the one rounding
             if (v < V) {
-                if (better(val, v, bv, bi)) {
-                    bv = val;
-                    bi = v;
+                if constexpr (kTopK == 0) {       // (the sampled epilogue's winner is its list's rank 0)
+                    if (better(val, v, bv, bi)) {
+                        bv = val;
+                        bi = v;
+                    }
                 }
                 if constexpr (kTopK > 0) {
                     key = order_key(val, v);
@@ -1114,7 +1116,8 @@ verify_kernel(Args a)
         flush_cand();
 
     // ---------------- per-workgroup best per token
-    row_best16(bv, bi);
+    if constexpr (kTopK == 0)
+        row_best16(bv, bi);
     if constexpr (kTopK > 0) {
         // lane n16 = j publishes the rank-j key of the workgroup's list;
         // the 16 lanes' (max, sum) pairs combine (fixed rotations) and lane
