@@ -476,11 +476,14 @@ __device__ __forceinline__ uint64_t lse_pack(float m, float s)
 // each 16-lane group loads pair j of row `row` (all loads in flight at once)
 // and a fixed sequence of row rotations combines them; every lane of the
 // group ends with the same pair.  Called by all lanes of the wave.
-__device__ __forceinline__ void lse_gather16(const uint64_t *pairs, int n, int M, int row, float &m, float &s)
+__device__ __forceinline__ uint64_t lse_load16(const uint64_t *pairs, int n, int M, int row)
 {
     const int j = threadIdx.x & 15;
-    const uint64_t pr = __hip_atomic_load(&pairs[(size_t)(j < n ? j : 0) * M + row], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(&pairs[(size_t)(j < n ? j : 0) * M + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void lse_combine16(uint64_t pr, int n, float &m, float &s)
+{
+    const int j = threadIdx.x & 15;
     m = j < n ? __uint_as_float((uint32_t)pr) : -__builtin_huge_valf();
     s = j < n ? __uint_as_float((uint32_t)(pr >> 32)) : 0.0f;
     row_lse16(m, s);
@@ -1179,9 +1182,11 @@ verify_kernel(Args a)
         if (!s_last)
             return;
         {
+            const int m = 2 * wave + (lane >> 5);
+            // the pairs' loads go out with the lists' (one round trip)
+            const uint64_t lse_pr = kLse ? lse_load16(a.part_lse + (size_t)16 * grp * M, gsz, M, m < M ? m : 0) : 0;
             const unsigned long long mine = merge_topk_lists<kTopK>(a.part_topk + (size_t)16 * grp * M * kTopK,
                                                                     gsz, M, lane);
-            const int m = 2 * wave + (lane >> 5);
             if (m < M && ((lane >> 4) & 1) == 0 && n16 < kTopK)
                 __hip_atomic_store(&a.group_topk[((size_t)grp * M + m) * kTopK + n16], mine,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1189,7 +1194,7 @@ verify_kernel(Args a)
                 // lane n16 of the token's 16-lane group loads workgroup n16's
                 // pair; fixed row rotations combine the 16
                 float gm, gs;
-                lse_gather16(a.part_lse + (size_t)16 * grp * M, gsz, M, m < M ? m : 0, gm, gs);
+                lse_combine16(lse_pr, gsz, gm, gs);
                 if (m < M && (lane & 31) == 0)
                     __hip_atomic_store(&a.group_lse[(size_t)grp * M + m], lse_pack(gm, gs), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
@@ -1306,14 +1311,25 @@ verify_kernel(Args a)
         // sampling at temperature tau): lane j of the token's first 16-lane
         // group holds rank j; sums are fixed rotations over the 16 lanes.
         const int n_grp = (G + 15) / 16;
-        const unsigned long long mine = merge_topk_lists<kTopK>(a.group_topk, n_grp, M, lane);
         const int m = 2 * wave + (lane >> 5);
         const int slot = lane & 31;                   // 0..15: first group of the token
         const int mm = m < M ? m : M - 1;
         const int T = a.T;
         const int req = mm / T, t = mm % T;
         const bool drafted = t < T - 1;
-        const int d = drafted ? s_draft[req * (T - 1) + t] : -1;
+        const int di = drafted ? req * (T - 1) + t : 0;
+        // every load of this stage is issued before the lists' (one round trip)
+        const float u_d = drafted ? a.unif[di] : 1.0f, q_d = drafted ? a.dprob[di] : 1.0f;
+        uint64_t lse_pr = 0;
+        int seen_d = 0;
+        float logit_d = 0.0f;
+        if constexpr (kLse) {
+            lse_pr = lse_load16(a.group_lse, n_grp, M, mm);
+            seen_d = __hip_atomic_load(&a.draft_seen[mm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            logit_d = __hip_atomic_load(&a.draft_logit[mm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const unsigned long long mine = merge_topk_lists<kTopK>(a.group_topk, n_grp, M, lane);
+        const int d = drafted ? s_draft[di] : -1;
         const float hv = key_value(mine);
         const int hi = key_index(mine);
         if (slot == 0 && m < M) {                     // rank 0: the greedy winner
@@ -1334,7 +1350,7 @@ verify_kernel(Args a)
         float lse = 0.0f;
         if constexpr (kLse) {
             float gm, gs;
-            lse_gather16(a.group_lse, n_grp, M, mm, gm, gs);
+            lse_combine16(lse_pr, n_grp, gm, gs);
             lse = (gm + __log2f(gs)) * 0.6931471805599453f;
         }
         if (slot == 0 && m < M) {
@@ -1342,19 +1358,13 @@ verify_kernel(Args a)
                 a.lse_out[m] = lse;
             int ok = 0;
             if (drafted) {
-                const int di = req * (T - 1) + t;
                 float p;
-                if (!kLse || a.top_k > 0) {
+                if (!kLse || a.top_k > 0)
                     p = e_d / sum;
-                } else {
-                    const bool seen = __hip_atomic_load(&a.draft_seen[m], __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT) != 0;
-                    p = seen ? expf(__hip_atomic_load(&a.draft_logit[m], __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT) / a.tau - lse)
-                             : 0.0f;
-                }
+                else
+                    p = seen_d != 0 ? expf(logit_d / a.tau - lse) : 0.0f;
                 a.p_draft[di] = p;
-                ok = a.unif[di] * a.dprob[di] < p;
+                ok = u_d * q_d < p;
             }
             s_accept[m] = ok;
             if constexpr (kLse)
