@@ -257,6 +257,31 @@ def test_sampled_int_exact_bitexact(vh, oracle_mod):
     check(g, o, lg, d, q, u, R, T, k, 1.0)
 
 
+@pytest.mark.parametrize("k,H", [(16, 512), (8, 5120), (16, 7296)])
+def test_sampled_monotone_logits(vh, oracle_mod, k, H):
+    """Head rows reordered so that token 0's logits rise along the vocabulary
+    (every tile's keys beat the list: the candidate buffer fills and is
+    sorted into the list tile after tile), token 1's (the negated hidden
+    state, exact) fall (no candidates after the first tile), token 2 random.
+    H = 7296 takes the direct-insertion path (no LDS room for the buffer)."""
+    R, T, V = 1, 3, 6000
+    say(f"monotone logits k={k} H={H}")
+    inp = synth.uniform_inputs(R * T, V, H, seed=k + H)
+    x = inp["hidden"].reshape(R * T, H).copy()
+    x[1] = x[0] ^ np.uint16(0x8000)                    # exact negation of token 0
+    lg0 = oracle_mod.logits(x[:1], inp["packed"], inp["scales"], 1, V, H)
+    order = np.argsort(lg0[0], kind="stable")          # ascending logits of token 0
+    packed = inp["packed"].reshape(V, H // 2)[order].copy()
+    inp = dict(hidden=x, packed=packed, scales=inp["scales"])
+    lg = oracle_mod.logits(x, packed, inp["scales"], R * T, V, H)
+    assert np.all(np.diff(lg[0].astype(np.float64)) >= 0)
+    d, q, u = make_drafts(lg, R, T, k, seed=3)
+    o = sm.verify_sampled(x, packed, inp["scales"], d, q, u, R, T, V, H, k, 1.0)
+    g = run(vh, inp, d, q, u, R, T, V, H, k, 1.0)
+    st = check(g, o, lg, d, q, u, R, T, k, 1.0)
+    say(f"monotone stats {st}")
+
+
 def test_k1_is_greedy_acceptance(vh):
     """top_k = 1: the argmax has probability 1, every other token 0, so with
     draft probabilities 1 and uniforms below 1 the sampled count equals the
