@@ -610,6 +610,18 @@ __device__ __forceinline__ void split_limbs(const float (&xs)[16], int e, uint32
     }
 }
 
+// Accepted-prefix lengths from one wave's ballot of per-row decisions (bit
+// r*T + t: draft t of request r accepted; R*T <= 64): request r accepts up
+// to its first rejected draft.  Lane r < R writes n_acc[r].
+__device__ __forceinline__ void accept_from_ballot(unsigned long long bits, int T, int R, int lane, int32_t *n_acc)
+{
+    if (lane < R) {
+        const unsigned long long drafts = (1ull << (T - 1)) - 1ull;     // T - 1 <= 15 draft bits
+        const unsigned long long rb = (bits >> (lane * T)) & drafts;
+        n_acc[lane] = rb == drafts ? T - 1 : __builtin_ctzll(~rb);
+    }
+}
+
 // ---------------------------------------------------------------- stage_kernel
 // One workgroup per token slot tau < kP.  Thread c owns the 16-channel chunk
 // c of the token's row: it loads x and s for its chunk once, the block finds
@@ -698,7 +710,6 @@ verify_kernel(Args a)
     struct Merge {
         float fv[kWaves][kMaxRows];
         int fi[kWaves][kMaxRows];
-        int arg[kMaxRows];
         int draft[kMaxRows];
         int accept[kMaxRows];
         int last;
@@ -721,7 +732,6 @@ verify_kernel(Args a)
     Merge &mg = *reinterpret_cast<Merge *>(&lds.ring[0][0]);
     auto &s_fv = mg.fv;
     auto &s_fi = mg.fi;
-    auto &s_arg = mg.arg;
     auto &s_draft = mg.draft;
     auto &s_accept = mg.accept;
     auto &s_last = mg.last;
@@ -1273,37 +1283,37 @@ verify_kernel(Args a)
             s_draft[threadIdx.x] = dft;
     }
     __syncthreads();
-    if (kTopK == 0 && threadIdx.x < (unsigned)M) {
-        const int m = threadIdx.x;
-        float fv[kWaves];
-        int fi[kWaves];
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            fv[w] = s_fv[w][m];
-            fi[w] = s_fi[w][m];
-        }
-        float v0 = fv[0];
-        int i0 = fi[0];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w)
-            if (better(fv[w], fi[w], v0, i0)) {
-                v0 = fv[w];
-                i0 = fi[w];
-            }
-        const int id = a.vmap ? a.vmap[i0] : i0;    // row -> token id
-        a.logits_max[m] = v0;
-        a.argmax[m] = id;
-        s_arg[m] = id;
-    }
-    __syncthreads();
     if constexpr (kTopK == 0) {
-        if (threadIdx.x < (unsigned)a.R) {
-            const int req = threadIdx.x;
+        // wave 0 (all M <= 16 rows): thread m takes row m's winner, and the
+        // acceptance of every request comes from one ballot of the
+        // draft matches
+        if (threadIdx.x < 64) {
+            const int m = threadIdx.x;
             const int T = a.T;
-            int n = 0;
-            while (n < T - 1 && s_arg[req * T + n] == s_draft[req * (T - 1) + n])
-                ++n;
-            a.n_acc[req] = n;
+            bool match = false;
+            if (m < M) {
+                float fv[kWaves];
+                int fi[kWaves];
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    fv[w] = s_fv[w][m];
+                    fi[w] = s_fi[w][m];
+                }
+                float v0 = fv[0];
+                int i0 = fi[0];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w)
+                    if (better(fv[w], fi[w], v0, i0)) {
+                        v0 = fv[w];
+                        i0 = fi[w];
+                    }
+                const int id = a.vmap ? a.vmap[i0] : i0;    // row -> token id
+                a.logits_max[m] = v0;
+                a.argmax[m] = id;
+                const int req = m / T, t = m % T;
+                match = t < T - 1 && id == s_draft[req * (T - 1) + t];
+            }
+            accept_from_ballot(__ballot(match), T, a.R, m, a.n_acc);
         }
     } else {
         // Sampled epilogue, final merge over the group lists, then the
@@ -1371,13 +1381,9 @@ verify_kernel(Args a)
                 __hip_atomic_store(&a.draft_seen[m], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
-        if (threadIdx.x < (unsigned)a.R) {
-            const int r = threadIdx.x;
-            int n = 0;
-            while (n < T - 1 && s_accept[r * T + n])
-                ++n;
-            a.n_acc[r] = n;
-        }
+        if (threadIdx.x < 64)
+            accept_from_ballot(__ballot((int)threadIdx.x < M && s_accept[threadIdx.x] != 0), T, a.R,
+                               (int)threadIdx.x, a.n_acc);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
