@@ -75,16 +75,16 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_062_083, write=74_944, source="int4vh.hip",
-                     source_sha256="e263d9e803ddd9f3ee0daffbc1d039eba6a723fb4c6af00b4245867d99c99358"),
-    "full_t16_top16": dict(read=391_614_887, write=568_576, source="int4vh.hip",
-                           source_sha256="e263d9e803ddd9f3ee0daffbc1d039eba6a723fb4c6af00b4245867d99c99358"),
-    "full_t16_top0": dict(read=391_385_003, write=358_912, source="int4vh.hip",
-                          source_sha256="e263d9e803ddd9f3ee0daffbc1d039eba6a723fb4c6af00b4245867d99c99358"),
-    "batch": dict(read=683_949_767, write=1_062_176, source="int4vh.hip",
-                  source_sha256="e263d9e803ddd9f3ee0daffbc1d039eba6a723fb4c6af00b4245867d99c99358"),
-    "draft_vocab": dict(read=21_338_003, write=17_536, source="int4vh.hip",
-                        source_sha256="e263d9e803ddd9f3ee0daffbc1d039eba6a723fb4c6af00b4245867d99c99358"),
+    "full_t16": dict(read=391_062_626, write=74_944, source="int4vh.hip",
+                     source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+    "full_t16_top16": dict(read=391_666_820, write=568_576, source="int4vh.hip",
+                           source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+    "full_t16_top0": dict(read=391_444_404, write=358_912, source="int4vh.hip",
+                          source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+    "batch": dict(read=683_929_301, write=1_062_176, source="int4vh.hip",
+                  source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+    "draft_vocab": dict(read=21_333_652, write=17_536, source="int4vh.hip",
+                        source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
