@@ -76,15 +76,15 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
     "full_t16": dict(read=391_062_626, write=74_944, source="int4vh.hip",
-                     source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+                     source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
     "full_t16_top16": dict(read=391_666_820, write=568_576, source="int4vh.hip",
-                           source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+                           source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
     "full_t16_top0": dict(read=391_444_404, write=358_912, source="int4vh.hip",
-                          source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+                          source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
     "batch": dict(read=683_929_301, write=1_062_176, source="int4vh.hip",
-                  source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+                  source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
     "draft_vocab": dict(read=21_333_652, write=17_536, source="int4vh.hip",
-                        source_sha256="15dbc3eab2e4c2a2e1503a2444b5d734dd4970d2277b287e78b047f548ad51bd"),
+                        source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }

@@ -10,7 +10,8 @@
 // positions are from "HyperQwen on one RTX 3090: a first-time developer's
 // guide to the 381-token claim", "What actually became faster?".
 //
-// Two launches on the caller's stream:
+// Two launches on the caller's stream (one for a block of one or two rows,
+// whose staging runs inside verify_kernel):
 //
 //  stage_kernel  turns hidden*scale (exact in binary32) into a 24-bit
 //      fixed-point code per token (power-of-two step from the token's largest
@@ -30,13 +31,14 @@
 //      call.  A weight nibble becomes the int8 value 16*q by moving it to the
 //      high half of a byte (two bit operations per 8 weights) and
 //      v_mfma_i32_16x16x64_i8 accumulates exactly in int32.  Each wave
-//      combines its limbs (weights 2^16, 2^8, 1) into int64 partial sums and
-//      stores them in LDS; after the next barrier the lanes that own a token
-//      add the 8 waves' partials -- integer addition, exact and independent of
-//      order -- and round the logit to binary32 once.  Each wave folds two
-//      tokens' logits into a running argmax.  The last
-//      workgroup to finish (atomic ticket) merges the per-workgroup winners,
-//      writes the outputs, counts accepted drafts and resets the ticket.
+//      combines its limbs (weights 2^16, 2^8, 1) into partial sums -- integers
+//      below 2^44, held exactly in binary64 -- and stores them in LDS; after
+//      the next barrier the lanes that own a token add the 8 waves' partials
+//      (exact, so independent of order) and round the logit to binary32 once.
+//      Each wave folds two tokens' logits into a running argmax.  The last
+//      workgroup to finish (two-level atomic ticket) merges the per-workgroup
+//      winners, writes the outputs, counts accepted drafts and resets the
+//      tickets.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
