@@ -1160,17 +1160,26 @@ verify_kernel(Args a)
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if constexpr (kTopK == 0) {
-        // the last workgroup of each group of 16 takes the top-level ticket
+        // With 8 or more tiles per workgroup the workgroups finish spread over
+        // microseconds and one ticket does not queue: the last one takes a
+        // single round trip.  Otherwise they finish together, and the last
+        // workgroup of each group of 16 takes the top-level ticket.
         if (threadIdx.x == 0) {
-            const int grp = b / kGroupWgs;
-            const int gsz = min(kGroupWgs, G - kGroupWgs * grp);
-            uint32_t *gt = a.group_ticket + (size_t)grp * kTicketStride;
-            bool last = __hip_atomic_fetch_add(gt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                        (uint32_t)(gsz - 1);
-            if (last) {
-                __hip_atomic_store(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            bool last;
+            if (a.n_tiles >= 8 * G) {
                 last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                       (uint32_t)((G + kGroupWgs - 1) / kGroupWgs - 1);
+                       (uint32_t)(G - 1);
+            } else {
+                const int grp = b / kGroupWgs;
+                const int gsz = min(kGroupWgs, G - kGroupWgs * grp);
+                uint32_t *gt = a.group_ticket + (size_t)grp * kTicketStride;
+                last = __hip_atomic_fetch_add(gt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                       (uint32_t)(gsz - 1);
+                if (last) {
+                    __hip_atomic_store(gt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                           (uint32_t)((G + kGroupWgs - 1) / kGroupWgs - 1);
+                }
             }
             s_last = last;
         }
