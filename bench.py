@@ -75,16 +75,16 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_062_626, write=74_944, source="int4vh.hip",
-                     source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
-    "full_t16_top16": dict(read=391_666_820, write=568_576, source="int4vh.hip",
-                           source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
-    "full_t16_top0": dict(read=391_444_404, write=358_912, source="int4vh.hip",
-                          source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
-    "batch": dict(read=683_929_301, write=1_062_176, source="int4vh.hip",
-                  source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
-    "draft_vocab": dict(read=21_333_652, write=17_536, source="int4vh.hip",
-                        source_sha256="b099f13424595a67fb05370d730ec218541f9df2cab4157e2d37de1c12e6609c"),
+    "full_t16": dict(read=391_063_233, write=73_920, source="int4vh.hip",
+                     source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+    "full_t16_top16": dict(read=391_668_706, write=568_576, source="int4vh.hip",
+                           source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+    "full_t16_top0": dict(read=391_444_478, write=358_912, source="int4vh.hip",
+                          source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+    "batch": dict(read=683_934_761, write=1_062_176, source="int4vh.hip",
+                  source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+    "draft_vocab": dict(read=21_341_587, write=17_536, source="int4vh.hip",
+                        source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
