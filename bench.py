@@ -76,15 +76,15 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
     "full_t16": dict(read=391_063_233, write=73_920, source="int4vh.hip",
-                     source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+                     source_sha256="eb7be2780233b7141f13b10787f40768d42bbf062c5e3d25d403fe8f6e6da1d2"),
     "full_t16_top16": dict(read=391_668_706, write=568_576, source="int4vh.hip",
-                           source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+                           source_sha256="eb7be2780233b7141f13b10787f40768d42bbf062c5e3d25d403fe8f6e6da1d2"),
     "full_t16_top0": dict(read=391_444_478, write=358_912, source="int4vh.hip",
-                          source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+                          source_sha256="eb7be2780233b7141f13b10787f40768d42bbf062c5e3d25d403fe8f6e6da1d2"),
     "batch": dict(read=683_934_761, write=1_062_176, source="int4vh.hip",
-                  source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+                  source_sha256="eb7be2780233b7141f13b10787f40768d42bbf062c5e3d25d403fe8f6e6da1d2"),
     "draft_vocab": dict(read=21_341_587, write=17_536, source="int4vh.hip",
-                        source_sha256="185caaefbc488692a793d245084b562d614f1d6590cfd0fb42e87eca26d9a636"),
+                        source_sha256="eb7be2780233b7141f13b10787f40768d42bbf062c5e3d25d403fe8f6e6da1d2"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }

@@ -101,8 +101,9 @@ constexpr int kStageThreads = 512;        // threads of stage_kernel (one 16-cha
 constexpr int kBatchMaxRows = 4096;       // rows per launch of the batch path
 
 // Workspace layout (bytes from the 256-byte aligned base).  The control block
-// (ticket and per-row keys) is zeroed by workspace_init and left zeroed by
-// every call; the rest is written before it is read.
+// (tickets, per-row keys, the sampled epilogue's draft flags) is zeroed by
+// workspace_init and left zeroed by every call; the rest is written before it
+// is read.
 constexpr size_t kWsTicket = 0;                                   // uint32 ticket
 constexpr size_t kWsKeys = 256;                                   // uint64 [4096] batch winner keys
 // Atomics on one 128-byte line serialise at the memory side (about 13 ns
@@ -707,8 +708,8 @@ verify_kernel(Args a)
     constexpr int kGroups = Slots<kP>::kGroups;
     constexpr int kTileBytes = kUnits * kWaves * 1024;     // LDS image of one tile (max H)
     // All LDS lives in one object: the weight ring, then the per-wave
-    // partial sums (int64 per D row and column, two buffers).  The final
-    // merge reuses the ring once it is dead.
+    // partial sums (exact integers held in binary64, per D row and column,
+    // two buffers).  The final merge reuses the ring once it is dead.
     struct Merge {
         float fv[kWaves][kMaxRows];
         int fi[kWaves][kMaxRows];
@@ -1405,7 +1406,7 @@ verify_kernel(Args a)
 // Blocks of more than 16 rows (up to 4096: many requests sharing one head).
 // The contraction is then a GEMM of (token, limb) rows against the head,
 // 3M x H times H x V, on the same int8 MFMA and with the same numerics as the
-// single-block kernels (identical codes, exact int32 / int64 sums, one
+// single-block kernels (identical codes, exact integer sums, one
 // rounding), so a row's results do not depend on the path or the batch it ran
 // in.  The step count grows with M: at M = 256 the 16x16x64 int8 MFMAs, not
 // the weight stream, bound the call.
