@@ -233,6 +233,20 @@ __device__ __forceinline__ void lds_load3_u64(const void *p0, const void *p1, co
                  : "memory");
 }
 
+// Element `hi` (0 or 1) of a wave-uniform pair of int32 in global memory,
+// loaded through the scalar unit and complete on return (it counts against
+// lgkmcnt only, so no vector load in flight is waited for).
+__device__ __forceinline__ int load_exp_pair(const int32_t *p, int hi)
+{
+    unsigned long long xy;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=s"(xy)
+                 : "s"(p)
+                 : "memory");
+    return (int)(uint32_t)(hi ? xy >> 32 : xy);
+}
+
 __device__ __forceinline__ void lds_store_u32(void *p, uint32_t v)
 {
     asm volatile("ds_write_b32 %0, %1" ::"v"(lds_offset(reinterpret_cast<unsigned long long *>(p))), "v"(v)
@@ -765,11 +779,14 @@ verify_kernel(Args a)
         const int jj = min(wave * kUnits + m, a.n_units - 1);
         loff[m] = (unsigned int)(jj * 1024 + (lane ^ (jj & 7)) * 16);
     }
-    auto issue_tile = [&](int k) {
+    // The first kRing tiles go out without the branch (clamped addresses
+    // throughout): the compiler then counts the copies in flight exactly and
+    // does not wait for all of them before the first use of the fragments.
+    auto issue_tile = [&](int k, bool branch_free = false) {
         const int tile = b + k * G;
         const unsigned long long base = (unsigned long long)tile * tile_bytes;
         uint8_t *dst = s_ring[k % kRing];
-        if (base + span_bytes <= a.w_bytes) {                // all of the tile's copies inside the head
+        if (!branch_free && base + span_bytes <= a.w_bytes) {   // all of the tile's copies inside the head
             const uint8_t *src = a.w + base;
 #pragma unroll
             for (int m = 0; m < kUnits; ++m) {
@@ -790,6 +807,11 @@ verify_kernel(Args a)
     const bool rlane = lane < 32 && rtok < M;
     i32x4 afr[kUnits][2][kGroups];
     int rexp;
+    // sampled epilogue: the draft id of the lane's token (loaded ahead of the
+    // weight copies, like every other register the main loop reads)
+    int my_draft = -1;
+    if (kTopK > 0 && rlane && a.T > 1 && (rtok % a.T) < a.T - 1)
+        my_draft = a.draft[(rtok / a.T) * (a.T - 1) + rtok % a.T];
     if constexpr (!kFused) {
         // from stage_kernel, in the workspace
 #pragma unroll
@@ -799,11 +821,17 @@ verify_kernel(Args a)
 #pragma unroll
                 for (int g = 0; g < kGroups; ++g)
                     afr[i][t][g] = __builtin_bit_cast(i32x4, a.frag[frag_index<kP, kUnits>(wave, i, t, g, lane)]);
-        rexp = a.exps[rtok < M ? rtok : 0] - 4;              // weights carry a factor 16
+        // the step exponents of the wave's two tokens, by a scalar load (a
+        // vector load here would make the compiler wait for every weight copy
+        // in flight where it is first used); lanes of tokens >= M never use
+        // theirs
+        rexp = load_exp_pair(a.exps + 2 * wave, (lane >> 4) & 1) - 4;   // weights carry a factor 16
+        // the prologue tiles, unconditional like the first step's (a tile
+        // past the head reads clamped bytes into a ring slot that is never
+        // used; every copy has landed before the workgroup publishes)
 #pragma unroll
         for (int k = 0; k < kRing - 1; ++k)
-            if (k < n_my)
-                issue_tile(k);
+            issue_tile(k, true);
     } else {
         // Staging done here for M <= 2 rows.  The scale row and the hidden
         // rows are copied into the last ring slot (unused until the main loop
@@ -836,7 +864,7 @@ verify_kernel(Args a)
         // count below is exactly this wave's weight copies
 #pragma unroll
         for (int k = 0; k < kRing - 1; ++k)
-            issue_tile(k);
+            issue_tile(k, true);
         __builtin_amdgcn_s_waitcnt(waitcnt_vm((kRing - 1) * kUnits));
         barrier_no_fence();
 
@@ -961,8 +989,8 @@ verify_kernel(Args a)
     float bv = -__builtin_huge_valf();
     int bi = 0x7FFFFFFF;
     // sampled epilogue: the token's distributed top-k list (lanes 0-15: token
-    // 2*wave, lanes 16-31: token 2*wave+1; rank = n16), the lane's running
-    // (max, sum) of exp2(logit * log2(e) / tau), and the token's draft id
+    // 2*wave, lanes 16-31: token 2*wave+1; rank = n16) and the lane's running
+    // (max, sum) of exp2(logit * log2(e) / tau)
     unsigned long long dl = 0ull;
     float lm = -__builtin_huge_valf(), ls = 0.0f;
     const float zscale = 1.4426950408889634f / a.tau;
@@ -978,9 +1006,6 @@ verify_kernel(Args a)
             cnt1 = 0;
         }
     };
-    int my_draft = -1;
-    if (kTopK > 0 && rlane && a.T > 1 && (rtok % a.T) < a.T - 1)
-        my_draft = a.draft[(rtok / a.T) * (a.T - 1) + rtok % a.T];
     // Rows of D that hold limbs of token t are t, t + kP, t + 2*kP (those
     // with a limb index below 3).  Every lane loads (clamped to a valid
     // token) so the loads are straight-line and all in flight together.
@@ -1067,13 +1092,19 @@ verify_kernel(Args a)
     };
 
     // ---------------- main loop over this workgroup's tiles
-    for (int k = 0; k < n_my; ++k) {
+    // One step per tile.  The first step runs ahead of the loop: the
+    // compiler waits for every copy in flight at the entry of a loop that
+    // uses registers loaded before it (the activation fragments), which would
+    // hold tile 0 until tile 1 has landed and tile 2 back until then; peeled,
+    // the step's own count of copies in flight covers the fragments.
+    auto step = [&](int k) {
         // this wave's copies of tile k are done (later tiles may be in flight);
         // after the barrier every wave's copies are, and tile k-1's partial
         // sums are complete in s_part
-        // copies issued after tile k's: min(kRing - 2, n_my - 1 - k) tiles
+        // copies issued after tile k's: min(kRing - 2, n_my - 1 - k) tiles,
+        // kRing - 2 at the first step (the prologue is unconditional)
         static_assert(kRing >= 2 && kRing <= 4, "ring depth");
-        const int later = min(kRing - 2, n_my - 1 - k);
+        const int later = k == 0 ? kRing - 2 : min(kRing - 2, n_my - 1 - k);
         if (later >= 2)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kUnits));
         else if (later == 1)
@@ -1082,7 +1113,9 @@ verify_kernel(Args a)
             __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         barrier_no_fence();
-        if (k + kRing - 1 < n_my)
+        if (k == 0)                                // (straight-line first step)
+            issue_tile(kRing - 1, true);
+        else if (k + kRing - 1 < n_my)
             issue_tile(k + kRing - 1);
 
         const uint8_t *tile = s_ring[k % kRing];
@@ -1124,7 +1157,10 @@ verify_kernel(Args a)
             // rows of tokens >= M hold zero activation codes, so val is 0
             lds_store_u64(&s_part[k & 1][wave][grp * 4 + r4][n16], (unsigned long long)__double_as_longlong(val));
         }
-    }
+    };
+    step(0);
+    for (int k = 1; k < n_my; ++k)
+        step(k);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     barrier_no_fence();
     reduce_tile(n_my - 1);
