@@ -821,17 +821,17 @@ verify_kernel(Args a)
 #pragma unroll
                 for (int g = 0; g < kGroups; ++g)
                     afr[i][t][g] = __builtin_bit_cast(i32x4, a.frag[frag_index<kP, kUnits>(wave, i, t, g, lane)]);
-        // the step exponents of the wave's two tokens, by a scalar load (a
-        // vector load here would make the compiler wait for every weight copy
-        // in flight where it is first used); lanes of tokens >= M never use
-        // theirs
-        rexp = load_exp_pair(a.exps + 2 * wave, (lane >> 4) & 1) - 4;   // weights carry a factor 16
         // the prologue tiles, unconditional like the first step's (a tile
         // past the head reads clamped bytes into a ring slot that is never
         // used; every copy has landed before the workgroup publishes)
 #pragma unroll
         for (int k = 0; k < kRing - 1; ++k)
             issue_tile(k, true);
+        // the step exponents of the wave's two tokens, by a scalar load once
+        // the copies are out (a vector load would make the compiler wait for
+        // every copy in flight where it is first used); lanes of tokens >= M
+        // never use theirs
+        rexp = load_exp_pair(a.exps + 2 * wave, (lane >> 4) & 1) - 4;   // weights carry a factor 16
     } else {
         // Staging done here for M <= 2 rows.  The scale row and the hidden
         // rows are copied into the last ring slot (unused until the main loop
@@ -1043,7 +1043,11 @@ verify_kernel(Args a)
                     a.logits_out[(size_t)rtok * V + v] = val;
             }
         }
-        if constexpr (kCBuf) {
+        if (kCBuf && k == 0) {
+            // the first tile: the lists are empty, so its 16 keys per token,
+            // sorted, are the lists (wave-uniform control flow)
+            dl = row_sort16(key, n16);
+        } else if constexpr (kCBuf) {
             // the tile's keys that beat the list's last kept rank go to the
             // token's candidate buffer; a full buffer is sorted and merged
             // into the list first (wave-uniform control flow)
