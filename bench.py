@@ -75,16 +75,16 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_054_108, write=73_920, source="int4vh.hip",
-                     source_sha256="14353d625aa97675c270b460fbaf57c1d131fe93fe1d9f7b4ae38bef645d2e05"),
-    "full_t16_top16": dict(read=391_653_336, write=568_576, source="int4vh.hip",
-                           source_sha256="14353d625aa97675c270b460fbaf57c1d131fe93fe1d9f7b4ae38bef645d2e05"),
-    "full_t16_top0": dict(read=391_430_692, write=358_912, source="int4vh.hip",
-                          source_sha256="14353d625aa97675c270b460fbaf57c1d131fe93fe1d9f7b4ae38bef645d2e05"),
-    "batch": dict(read=683_944_407, write=1_062_176, source="int4vh.hip",
-                  source_sha256="14353d625aa97675c270b460fbaf57c1d131fe93fe1d9f7b4ae38bef645d2e05"),
-    "draft_vocab": dict(read=21_338_260, write=17_536, source="int4vh.hip",
-                        source_sha256="14353d625aa97675c270b460fbaf57c1d131fe93fe1d9f7b4ae38bef645d2e05"),
+    "full_t16": dict(read=391_057_672, write=73_920, source="int4vh.hip",
+                     source_sha256="4b8c451422145163e42b29ebbc4afce0bc7cffe0dbe436f1f6c7a9e3261820ee"),
+    "full_t16_top16": dict(read=391_701_930, write=568_576, source="int4vh.hip",
+                           source_sha256="4b8c451422145163e42b29ebbc4afce0bc7cffe0dbe436f1f6c7a9e3261820ee"),
+    "full_t16_top0": dict(read=391_483_434, write=358_912, source="int4vh.hip",
+                          source_sha256="4b8c451422145163e42b29ebbc4afce0bc7cffe0dbe436f1f6c7a9e3261820ee"),
+    "batch": dict(read=683_938_251, write=1_062_176, source="int4vh.hip",
+                  source_sha256="4b8c451422145163e42b29ebbc4afce0bc7cffe0dbe436f1f6c7a9e3261820ee"),
+    "draft_vocab": dict(read=21_335_188, write=17_536, source="int4vh.hip",
+                        source_sha256="4b8c451422145163e42b29ebbc4afce0bc7cffe0dbe436f1f6c7a9e3261820ee"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
