@@ -75,6 +75,8 @@
  *                       V*H/2 >= 2^40 bytes)
  *   INT4VH_EHIP         a HIP runtime error; the text is in
  *                       verify_lm_head_int4_last_error()
+ *   INT4VH_ESCRATCH     (verify_lm_head_int4_batch_noalloc only) the shape
+ *                       needs more workspace than its static scratch holds
  */
 #ifndef INT4VH_H
 #define INT4VH_H
@@ -92,7 +94,8 @@ enum {
     INT4VH_EALIGN = -2,
     INT4VH_EWORKSPACE = -3,
     INT4VH_EHIP = -4,
-    INT4VH_EUNSUPPORTED = -5
+    INT4VH_EUNSUPPORTED = -5,
+    INT4VH_ESCRATCH = -6
 };
 
 /* Largest hidden size of this build. */
@@ -146,6 +149,30 @@ int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
                                     int32_t *n_accepted, float *logits_out, void *workspace,
                                     size_t workspace_bytes, void *stream, void *event_before,
                                     void *event_after);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the batch
+ * call with no workspace argument.  The library keeps one scratch array of
+ * INT4VH_SCRATCH_BYTES (16 MiB) per device in static device memory, created
+ * when the library's code object is loaded on that device and held until the
+ * process ends; this call allocates nothing and calls no allocating routine.
+ * Its control words are zeroed once per device by a small fill kernel on
+ * `stream` (under stream capture the fill is recorded into the graph, and the
+ * next uncaptured call issues it again); every call leaves them zeroed.
+ * Every call on one device shares that device's array, which keeps the last
+ * call's contents: calls that overlap in time on one GPU (two streams, two
+ * host threads, two graphs in flight) race and must be serialised by the
+ * caller.  Same arguments (minus the workspace), results and errors as
+ * verify_lm_head_int4_batch, plus INT4VH_ESCRATCH, returned before any GPU
+ * call, when the shape needs more workspace than the scratch holds
+ * (verify_lm_head_int4_workspace_bytes(R, T, V, H) > INT4VH_SCRATCH_BYTES:
+ * every call of up to 16 rows fits; at H = 5120, up to 1024 rows).  After an
+ * INT4VH_EHIP the next call zeroes the control words again. */
+#define INT4VH_SCRATCH_BYTES (16u << 20)
+int verify_lm_head_int4_batch_noalloc(const void *hidden, const uint8_t *packed_w, const void *scales,
+                                      const int32_t *draft_ids, int R, int T, int V, int H,
+                                      float *logits_max, int32_t *argmax_ids, int32_t *n_accepted,
+                                      float *logits_out, void *stream);
 
 /* A head whose rows are a subset of the vocabulary: the draft vocabulary of
  * "HyperQwen: 1,000 tok/s on a Single RTX 3090 Through Aggressive

@@ -5,7 +5,7 @@ Python entry points below marshal torch tensors into its C ABI.  Importing
 this package loads nothing; the library is loaded on the first call.
 """
 
-__all__ = ["verify", "verify_batch", "verify_mapped", "verify_sampled", "check_weights", "check_vocab_map",
+__all__ = ["verify", "verify_batch", "verify_batch_noalloc", "verify_mapped", "verify_sampled", "check_weights", "check_vocab_map",
            "workspace_bytes", "load_library",
            "requant_amax", "requant_scales", "requant_pack", "requantize", "context_copy"]
 

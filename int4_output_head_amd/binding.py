@@ -16,7 +16,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libint4vh.so")
 
-OK, EINVAL, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED = 0, -1, -2, -3, -4, -5
+OK, EINVAL, EALIGN, EWORKSPACE, EHIP, EUNSUPPORTED, ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 
 _lib = None
 _lock = threading.Lock()
@@ -45,6 +45,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         L.verify_lm_head_int4_batch_timed.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P,
                                                       P, sz, P, P, P]
         L.verify_lm_head_int4_batch_timed.restype = i32
+        L.verify_lm_head_int4_batch_noalloc.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P,
+                                                        P]
+        L.verify_lm_head_int4_batch_noalloc.restype = i32
         L.verify_lm_head_int4_check_weights.argtypes = [P, i32, i32, P, P]
         L.verify_lm_head_int4_check_weights.restype = i32
         L.verify_lm_head_int4_status_string.argtypes = [i32]
@@ -200,6 +203,63 @@ def verify_batch(hidden, packed_w, scales, draft_ids=None, *, R: int | None = No
     if st != OK:
         _raise(st, "verify_lm_head_int4_batch")
     return (lmax, amax, nacc, lout) if logits else (lmax, amax, nacc)
+
+
+def verify_batch_noalloc(hidden, packed_w, scales, draft_ids=None, *, R: int | None = None,
+                         logits: bool = False, out=None):
+    """verify_batch through the entry point that allocates nothing
+    (verify_lm_head_int4_batch_noalloc: the library's static per-device
+    scratch replaces the workspace).  out=(logits_max, argmax_ids,
+    n_accepted[, logits]) supplies preallocated outputs (as a caller under
+    graph capture would); otherwise they are allocated here, by torch.  Calls
+    that overlap in time on one device race on the shared scratch."""
+    if hidden.dim() == 3:
+        R, T, H = hidden.shape
+        hidden = hidden.reshape(R * T, H)
+    else:
+        if R is None:
+            raise ValueError("R is required for a 2-D hidden tensor")
+        T = hidden.shape[0] // R
+        H = hidden.shape[1]
+    _check(hidden, "hidden", torch.float16, 2)
+    _check(packed_w, "packed_w", torch.uint8, 2)
+    _check(scales, "scales", torch.float16, 1)
+    V = packed_w.shape[0]
+    if packed_w.shape[1] * 2 != H or scales.shape[0] != H or hidden.shape[0] != R * T:
+        raise ValueError("shape mismatch between hidden, packed_w and scales")
+    dev = hidden.device
+    if T > 1:
+        if draft_ids is None:
+            raise ValueError("draft_ids is required when T > 1")
+        _check(draft_ids, "draft_ids", torch.int32)
+        if draft_ids.numel() != R * (T - 1):
+            raise ValueError("draft_ids must hold R*(T-1) ids")
+    else:
+        draft_ids = None
+    M = R * T
+    if out is not None:
+        lmax, amax, nacc = out[0], out[1], out[2]
+        lout = out[3] if len(out) > 3 else None
+        _check(lmax, "logits_max", torch.float32)
+        _check(amax, "argmax_ids", torch.int32)
+        _check(nacc, "n_accepted", torch.int32)
+        if lmax.numel() != M or amax.numel() != M or nacc.numel() != R:
+            raise ValueError("output sizes do not match R*T rows and R requests")
+        if lout is not None:
+            _check(lout, "logits", torch.float32)
+            if lout.numel() != M * V:
+                raise ValueError("logits must hold R*T*V values")
+    else:
+        lmax = torch.empty(M, dtype=torch.float32, device=dev)
+        amax = torch.empty(M, dtype=torch.int32, device=dev)
+        nacc = torch.empty(R, dtype=torch.int32, device=dev)
+        lout = torch.empty((M, V), dtype=torch.float32, device=dev) if logits else None
+    st = load_library().verify_lm_head_int4_batch_noalloc(
+        _ptr(hidden), _ptr(packed_w), _ptr(scales), _ptr(draft_ids), R, T, V, H, _ptr(lmax),
+        _ptr(amax), _ptr(nacc), _ptr(lout), _stream_ptr(dev))
+    if st != OK:
+        _raise(st, "verify_batch_noalloc")
+    return (lmax, amax, nacc, lout) if lout is not None else (lmax, amax, nacc)
 
 
 def verify_mapped(hidden, packed_w, scales, vocab_ids, draft_ids=None, *, R: int | None = None,

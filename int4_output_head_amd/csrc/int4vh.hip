@@ -45,6 +45,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <string>
 
@@ -62,7 +63,7 @@ int hip_fail(hipError_t e, const char *what)
 }
 
 namespace {
-constexpr int kMaxDevices = 64;
+constexpr int kMaxDevices = kMaxDevicesPublic;
 int g_cu_count[kMaxDevices];
 std::once_flag g_cu_once[kMaxDevices];
 } // namespace
@@ -2056,15 +2057,16 @@ size_t workspace_need(int R, int T, int V, int H)
     return kWsFrag + n_mt * kRTbPerTile * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
 }
 
-int validate(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
-             int R, int T, int V, int H, const float *lmax, const int32_t *amax_ids,
-             const int32_t *nacc, const float *lout, const void *ws, size_t ws_bytes)
+// Every argument check except the workspace's (no GPU call).
+int validate_args(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
+                  int R, int T, int V, int H, const float *lmax, const int32_t *amax_ids,
+                  const int32_t *nacc, const float *lout)
 {
     if (R < 1 || T < 1 || T > INT4VH_MAX_T || V < 1 || H < 32 || (H % 32) != 0)
         return INT4VH_EINVAL;
     if ((long long)R * T > kBatchMaxRows)
         return INT4VH_EINVAL;
-    if (!hidden || !w || !scales || !lmax || !amax_ids || !nacc || !ws)
+    if (!hidden || !w || !scales || !lmax || !amax_ids || !nacc)
         return INT4VH_EINVAL;
     if (T > 1 && !draft)
         return INT4VH_EINVAL;
@@ -2074,7 +2076,21 @@ int validate(const void *hidden, const uint8_t *w, const void *scales, const int
         return INT4VH_EUNSUPPORTED;
     if (!aligned(hidden, 16) || !aligned(w, 16) || !aligned(scales, 16) || !aligned(lmax, 16) ||
         !aligned(amax_ids, 16) || !aligned(nacc, 4) || (draft && !aligned(draft, 4)) ||
-        (lout && !aligned(lout, 16)) || !aligned(ws, 256))
+        (lout && !aligned(lout, 16)))
+        return INT4VH_EALIGN;
+    return INT4VH_OK;
+}
+
+int validate(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
+             int R, int T, int V, int H, const float *lmax, const int32_t *amax_ids,
+             const int32_t *nacc, const float *lout, const void *ws, size_t ws_bytes)
+{
+    const int st = validate_args(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout);
+    if (st != INT4VH_OK)
+        return st;
+    if (!ws)
+        return INT4VH_EINVAL;
+    if (!aligned(ws, 256))
         return INT4VH_EALIGN;
     if (ws_bytes < workspace_need(R, T, V, H))
         return INT4VH_EWORKSPACE;
@@ -2247,6 +2263,62 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     return record_event(ev1, s, "event record after verify kernel");
 }
 
+// ---------------------------------------------------------------- static scratch
+// The workspace of verify_lm_head_int4_batch_noalloc: one array per device,
+// allocated when the code object is loaded and held until the process ends.
+// Host code never uses the array's name as an address (in host code it names
+// a host-side stand-in); it uses the device address from hipGetSymbolAddress,
+// taken once per device with that device current.
+constexpr size_t kScratchBytes = INT4VH_SCRATCH_BYTES;
+
+} // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+struct ScratchSlot {
+    std::once_flag once;
+    void *ptr = nullptr;
+    hipError_t err = hipSuccess;
+    std::atomic<bool> zeroed{false};   // control block zeroed by an uncaptured fill
+};
+ScratchSlot g_scratch[int4vh_detail::kMaxDevicesPublic];
+
+// The device address of `scratch` on device dev (the current device), with
+// its control block zeroed.  The zeroing is a fill kernel on the caller's
+// stream: under stream capture it becomes part of the graph (every replay
+// zeroes again), and the next uncaptured call issues it once more.  Every
+// verify call leaves the control block zeroed, so this is needed once per
+// device, and again after a call that failed.
+int scratch_for_device(int dev, hipStream_t s, char **out)
+{
+    if (dev < 0 || dev >= int4vh_detail::kMaxDevicesPublic)
+        return INT4VH_EUNSUPPORTED;
+    ScratchSlot &sl = g_scratch[dev];
+    std::call_once(sl.once, [&sl] { sl.err = hipGetSymbolAddress(&sl.ptr, HIP_SYMBOL(scratch)); });
+    if (sl.err != hipSuccess)
+        return hip_fail(sl.err, "hipGetSymbolAddress(scratch)");
+    if (!sl.ptr || !aligned(sl.ptr, 256))
+        return hip_fail(hipErrorInvalidSymbol, "scratch address");
+    if (!sl.zeroed.load(std::memory_order_acquire)) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        hipError_t e = hipStreamIsCapturing(s, &cs);
+        if (e != hipSuccess)
+            return hip_fail(e, "hipStreamIsCapturing");
+        const int n = (int)(kWsCtlBytes / sizeof(uint32_t));
+        hipLaunchKernelGGL(fill_zero_u32, dim3((n + 255) / 256), dim3(256), 0, s, static_cast<uint32_t *>(sl.ptr),
+                           n);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return hip_fail(e, "scratch zero launch");
+        if (cs == hipStreamCaptureStatusNone)
+            sl.zeroed.store(true, std::memory_order_release);
+    }
+    *out = static_cast<char *>(sl.ptr);
+    return INT4VH_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -2302,6 +2374,33 @@ int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
     return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
                          n_accepted, logits_out, workspace, workspace_bytes, stream, event_before,
                          event_after);
+}
+
+int verify_lm_head_int4_batch_noalloc(const void *hidden, const uint8_t *packed_w, const void *scales,
+                                      const int32_t *draft_ids, int R, int T, int V, int H,
+                                      float *logits_max, int32_t *argmax_ids, int32_t *n_accepted,
+                                      float *logits_out, void *stream)
+{
+    int st = validate_args(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
+                           n_accepted, logits_out);
+    if (st != INT4VH_OK)
+        return st;
+    if (workspace_need(R, T, V, H) > kScratchBytes)
+        return INT4VH_ESCRATCH;
+    int dev = 0;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = nullptr;
+    st = scratch_for_device(dev, s, &ws);
+    if (st != INT4VH_OK)
+        return st;
+    st = launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
+                       n_accepted, logits_out, ws, kScratchBytes, stream);
+    if (st == INT4VH_EHIP)
+        g_scratch[dev].zeroed.store(false, std::memory_order_release);   // zero again next time
+    return st;
 }
 
 int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, const void *scales,
@@ -2415,6 +2514,7 @@ const char *verify_lm_head_int4_status_string(int status)
     case INT4VH_EWORKSPACE: return "workspace too small";
     case INT4VH_EHIP: return "HIP runtime error";
     case INT4VH_EUNSUPPORTED: return "unsupported shape";
+    case INT4VH_ESCRATCH: return "shape needs more than the static scratch of the no-allocation entry point";
     default: return "unknown status";
     }
 }

@@ -9,6 +9,9 @@
 
 namespace int4vh_detail {
 
+// Largest device ordinal the library keeps per-device state for.
+constexpr int kMaxDevicesPublic = 64;
+
 // Text of the last INT4VH_EHIP error on the calling thread.
 extern __attribute__((visibility("hidden"))) thread_local std::string g_last_error;
 
