@@ -25,6 +25,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA peak, TOP/s
 SINGLE_BLOCK_ROWS = 16         # larger blocks run the MFMA-bound batch kernels
 METRIC = "int4 lm_head verify: weight GB/s (% HBM peak) and verified tokens/s at T=16"
+# what the path computes: int4 weights times 24-bit fixed-point activation
+# codes (x*s, exact in binary32, rounded to 24 bits), run as three int8 MFMA
+# limbs with exact integer sums, one rounding to binary32 per logit
+DTYPE = "int4 x int24 (3 int8 MFMA limbs, exact integer sums, fp32 logits)"
 
 
 def log(msg):
@@ -39,13 +43,26 @@ def stored_argmax(name):
         return json.load(f)
 
 
-def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap=None):
+def host_threads():
+    """Threads for the oracle on this host: the CPUs this process may run on,
+    capped by OMP_NUM_THREADS (the host share of one GPU where it is set)."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap=None, want_logits=False):
     """The oracle, as it is, on this host: whole verify steps of the same
     workload (bounded number of trials) -- the sampled oracle for top-k
-    sampling, the draft-vocabulary oracle for a mapped head."""
+    sampling, the draft-vocabulary oracle for a mapped head.  With
+    want_logits the first trial's logits are returned too (the oracle writes
+    them into the caller's array instead of a scratch one: the same work)."""
     from oracle import oracle, sampled, vocab_map
     from int4_output_head_amd import synth
     times = []
+    first = None
     for trial in trials:
         x = synth.make_hidden(cfg, trial)
         drafts = np.zeros((cfg.R, cfg.T - 1), np.int32)
@@ -58,15 +75,18 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
             vocab_map.verify_mapped(x, head["packed"], head["scales"], vmap, drafts, cfg.R, cfg.T,
                                     cfg.V, cfg.H, n_threads=n_threads)
         else:
-            oracle.verify(x, head["packed"], head["scales"], drafts, cfg.R, cfg.T, cfg.V, cfg.H,
-                          n_threads=n_threads)
+            o = oracle.verify(x, head["packed"], head["scales"], drafts, cfg.R, cfg.T, cfg.V, cfg.H,
+                              n_threads=n_threads, want_logits=want_logits and first is None)
+            if first is None:
+                first = o
         times.append(time.perf_counter() - t0)
     t = float(np.mean(times))
-    return dict(value=round(cfg.weight_bytes / t / 1e9, 4), unit="GB/s", cores=n_threads,
-                kind="oracle", seconds_per_step=round(t, 4),
-                verified_tok_s=round(cfg.M / t, 3),
-                sample=f"{len(trials)} whole verify steps of the same workload (all {cfg.M} rows x "
-                       f"{cfg.V} vocab rows), trial seeds {list(trials)}")
+    res = dict(value=round(cfg.weight_bytes / t / 1e9, 4), unit="GB/s", cores=n_threads,
+               kind="oracle", seconds_per_step=round(t, 6),
+               verified_tok_s=round(cfg.M / t, 3),
+               sample=f"{len(trials)} whole verify steps of the same workload (all {cfg.M} rows x "
+                      f"{cfg.V} vocab rows), trial seeds {trials[0]}..{trials[-1]}, mean per step")
+    return res, first
 
 
 # HBM bytes per launch of the main kernel, from two rocprofv3 runs (FETCH_SIZE,
@@ -90,6 +110,10 @@ MEASURED_TRAFFIC = {
 }
 
 
+TRAFFIC_NOTE = ("HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of this exact kernel "
+                "source (SHA-256 checked; summaries in profiles/), divided by this run's mean launch time")
+
+
 def measured_traffic(key, t_launch):
     import hashlib
     rec = MEASURED_TRAFFIC.get(key)
@@ -111,15 +135,18 @@ def roofline(cfg, t_launch, gbs, key=None):
     row, channel), 2*M*V*H int8 ops; the kernel executes three times that
     (three limbs per activation code), reported beside it."""
     traffic, traffic_bytes = measured_traffic(key or cfg.name, t_launch)
+    note = TRAFFIC_NOTE if traffic is not None else "no counter run for this kernel source"
     if cfg.M <= SINGLE_BLOCK_ROWS:
         return {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "traffic_bytes_per_launch": traffic_bytes}
+                "traffic_bytes_per_launch": traffic_bytes, "traffic_source": note,
+                "algorithmic_bytes_per_launch": cfg.weight_bytes}
     ops = 2.0 * cfg.M * cfg.V * cfg.H
     tops = ops / t_launch / 1e12
     return {"bound": "mfma", "achieved": round(tops, 2), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
             "frac": round(tops / INT8_PEAK_TOPS, 4), "traffic": traffic,
-            "traffic_unit": "GB/s", "traffic_bytes_per_launch": traffic_bytes,
+            "traffic_unit": "GB/s", "traffic_bytes_per_launch": traffic_bytes, "traffic_source": note,
+            "algorithmic_ops_per_launch": ops,
             "executed_int8_tops": round(3 * tops, 2),
             "executed_frac": round(3 * tops / INT8_PEAK_TOPS, 4),
             "weight_gb_s": round(gbs, 2)}
@@ -142,6 +169,8 @@ def calibration_copy(torch, dev):
 
 
 REQUANT = dict(V=151936, H=5120, N=4096)
+# oracle trials of the CPU baseline per workload (about 10-30 s of CPU work)
+CPU_TRIALS = {"tiny": 200, "draft_vocab": 100, "full_t8": 2, "full_t16": 2, "shard_t16": 8, "batch": 1}
 
 
 def bench_requant(args):
@@ -240,6 +269,62 @@ def bench_requant(args):
     print(json.dumps(result), flush=True)
 
 
+def bench_stream(args):
+    """The reference line for the weight stream: a plain read-only pass over a
+    buffer of the packed full-vocabulary head's size (388,956,160 B), with
+    two copies rotated so the 256 MB Infinity Cache cannot serve it; mode 0
+    loads into registers, mode 1 copies into LDS with the verify kernel's
+    instruction.  One step is one pass."""
+    import torch
+    from int4_output_head_amd import binding
+
+    dev = torch.device("cuda:0")
+    binding.load_library()
+    nbytes = CALIBRATION_COPY_BYTES
+    gen = torch.Generator(device=dev).manual_seed(0)
+    bufs = [torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev, generator=gen)
+            for _ in range(2)]
+    # the kernel reads every byte: the xor of its per-wave words is the xor
+    # of the buffer's 32-bit words (computed on the host)
+    out = binding.stream_read(bufs[0], 0)
+    torch.cuda.synchronize()
+    want = int(np.bitwise_xor.reduce(bufs[0].cpu().numpy().view(np.uint32)))
+    got = int(np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32)))
+    res = {}
+    for mode in (0, 1):
+        for i in range(max(args.warmup, 20)):
+            binding.stream_read(bufs[i % 2], mode, out=out)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for i in range(args.steps):
+            binding.stream_read(bufs[i % 2], mode, out=out, events=ev[i])
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) for a, b in ev]) * 1e-3
+        res[mode] = dict(us_mean=round(float(per.mean()) * 1e6, 3),
+                         us_p10=round(float(np.percentile(per, 10)) * 1e6, 3),
+                         us_p90=round(float(np.percentile(per, 90)) * 1e6, 3),
+                         GB_s=round(nbytes / float(per.mean()) / 1e9, 2))
+        log(f"stream mode {mode}: {res[mode]}")
+    best = max(res.values(), key=lambda r: r["GB_s"])
+    result = {
+        "metric": "read-only HBM stream of a head-sized buffer: GB/s (the weight stream's reference line)",
+        "value": best["GB_s"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(best["us_mean"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8 (read only)", "data": "synthetic",
+        "config": {"workload": f"read {nbytes} B once per step, 2 buffers rotated",
+                   "bytes": nbytes, "timing": "eager, HIP events around each kernel"},
+        "modes": {"registers (global_load_dwordx4)": res[0], "lds (global_load_lds_dwordx4)": res[1]},
+        "roofline": {"bound": "hbm", "achieved": best["GB_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(best["GB_s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": nbytes},
+        "parity_gate": {"xor_of_buffer_equal": got == want},
+        "cpu_baseline": None,
+        "cpu_baseline_note": "a measurement kernel with no oracle counterpart",
+    }
+    print(json.dumps(result), flush=True)
+
+
 def bench_context_copy(args):
     """The context-copy drafter on the workload of the wide verify block: a
     25,000-token synthetic prompt per request, a 16-token key whose tail
@@ -322,7 +407,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="full_t16")
     ap.add_argument("--copies", type=int, default=0, help="head copies to rotate (0: auto)")
-    ap.add_argument("--cpu-trials", type=int, default=2)
+    ap.add_argument("--cpu-trials", type=int, default=0, help="oracle trials of the CPU baseline (0: per workload)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--top-k", type=int, default=0,
                     help="sampled verification: top-k sampling with this k (0: greedy)")
@@ -344,6 +429,9 @@ def main():
     if args.config == "context_copy":
         bench_context_copy(args)
         return
+    if args.config == "stream":
+        bench_stream(args)
+        return
 
     import torch
     from int4_output_head_amd import binding, synth
@@ -357,7 +445,12 @@ def main():
     t0 = time.time()
     head = synth.make_head(cfg)
     log(f"head generated in {time.time() - t0:.1f}s")
-    copies = args.copies or max(2, -(-600_000_000 // cfg.weight_bytes))  # > 256 MB MALL
+    if args.copies:
+        copies = args.copies
+    elif cfg.weight_bytes < 4 << 20:
+        copies = 1        # fits one XCD's L2: the call is dispatch-bound, rotation cannot change that
+    else:
+        copies = max(2, -(-600_000_000 // cfg.weight_bytes))  # > 256 MB MALL
     w0 = torch.from_numpy(head["packed"]).to(dev)
     ws = [w0] + [w0.clone() for _ in range(copies - 1)]
     s = torch.from_numpy(head["scales"]).view(torch.float16).to(dev)
@@ -540,7 +633,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": DTYPE,
         "data": "synthetic",
         "config": {"workload": cfg.desc, "V": cfg.V, "H": cfg.H, "R": cfg.R, "T": cfg.T,
                    "head_copies_rotated": copies, "trials": n_trials,
@@ -569,12 +662,35 @@ def main():
         "parity_gate": gate,
     }
     if not args.no_cpu_baseline:
-        n_threads = min(16, os.cpu_count() or 1)
-        log(f"cpu baseline: oracle on {n_threads} threads, {args.cpu_trials} trials")
-        result["cpu_baseline"] = cpu_baseline(cfg, head, list(range(args.cpu_trials)), n_threads,
-                                              top_k=args.top_k if sampled else None,
-                                              temperature=args.temperature,
-                                              vmap=vmap_np)
+        n_threads = host_threads()
+        n_cpu = args.cpu_trials or CPU_TRIALS.get(cfg.name, 2)
+        log(f"cpu baseline: oracle on {n_threads} threads, {n_cpu} trials")
+        plain = not sampled and vmap_np is None
+        cb, first = cpu_baseline(cfg, head, list(range(n_cpu)), n_threads,
+                                 top_k=args.top_k if sampled else None, temperature=args.temperature,
+                                 vmap=vmap_np, want_logits=plain)
+        cb["cpu_count"] = os.cpu_count()
+        cb["affinity_cpus"] = len(os.sched_getaffinity(0))
+        cb["omp_num_threads"] = os.environ.get("OMP_NUM_THREADS")
+        if cfg.name in ("tiny", "draft_vocab"):
+            st, _ = cpu_baseline(cfg, head, list(range(n_cpu)), 1, vmap=vmap_np)
+            cb["single_thread"] = {k: st[k] for k in ("value", "unit", "cores", "seconds_per_step",
+                                                      "verified_tok_s", "sample")}
+        result["cpu_baseline"] = cb
+        if plain and first is not None and "logits" in first:
+            # the GPU's outputs and logits of trial 0 against the oracle's,
+            # element by element (the oracle ran with zero drafts: its
+            # acceptance count is recomputed for trial 0's drafts)
+            from tests import parity
+            d0 = ds[0].cpu().numpy() if ds[0] is not None else None
+            lmax0, ids0, nacc0, lg0 = binding.verify_batch(xs[0], ws[0], s, ds[0], logits=True, workspace=work)
+            torch.cuda.synchronize()
+            g = dict(logits_max=lmax0.cpu().numpy(), argmax_ids=ids0.cpu().numpy(),
+                     n_accepted=nacc0.cpu().numpy(), logits=lg0.cpu().numpy())
+            o0 = dict(first)
+            o0["n_accepted"] = parity.accept_from(o0["argmax_ids"], d0, cfg.R, cfg.T)
+            result["parity_gate"]["logits_trial0"] = parity.check(g, o0, cfg.R, cfg.T, d0)
+            log(f"trial 0 logits against the oracle: {result['parity_gate']['logits_trial0']}")
     print(json.dumps(result), flush=True)
 
 

@@ -7,7 +7,7 @@ this package loads nothing; the library is loaded on the first call.
 
 __all__ = ["verify", "verify_batch", "verify_batch_noalloc", "verify_mapped", "verify_sampled", "check_weights", "check_vocab_map",
            "workspace_bytes", "load_library",
-           "requant_amax", "requant_scales", "requant_pack", "requantize", "context_copy"]
+           "requant_amax", "requant_scales", "requant_pack", "requantize", "context_copy", "stream_read"]
 
 
 def __getattr__(name):

@@ -66,6 +66,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                         ctypes.c_float, P, P, P, P, P, P, P, P, sz,
                                                         P, P, P]
         L.verify_lm_head_int4_sampled_timed.restype = i32
+        # read-only streaming reference (include/int4vh_probe.h)
+        L.int4vh_stream_read.argtypes = [P, sz, i32, P, P, P, P]
+        L.int4vh_stream_read.restype = i32
         # context-copy drafter (include/int4vh_drafter.h)
         L.context_copy_propose.argtypes = [P, P, i32, P, i32, i32, i32, P, P, P, P, P]
         L.context_copy_propose.restype = i32
@@ -571,3 +574,26 @@ def context_copy(prompts, offsets, keys, *, n_min: int = 1, n_out: int = 8, even
     if st != OK:
         _raise(st, "context_copy_propose")
     return tok, cnt, end, ln
+
+
+PROBE_OUT_WORDS = 8192
+
+
+def stream_read(buf, mode: int = 0, *, out=None, events=None):
+    """Read the device tensor `buf` once (int4vh_stream_read): mode 0 loads
+    into registers, mode 1 copies into LDS like the verify kernel.  Returns
+    the per-wave words (uint32 as int32 [8192]); in mode 0 their xor is the
+    xor of the buffer's 32-bit words."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("buf must be a contiguous CUDA (HIP) tensor")
+    dev = buf.device
+    if out is None:
+        out = torch.zeros(PROBE_OUT_WORDS, dtype=torch.int32, device=dev)
+    nbytes = buf.numel() * buf.element_size()
+    stream = torch.cuda.current_stream(dev)
+    e0 = _event_handle(events[0], stream) if events else None
+    e1 = _event_handle(events[1], stream) if events else None
+    st = load_library().int4vh_stream_read(_ptr(buf), nbytes, int(mode), _ptr(out), _stream_ptr(dev), e0, e1)
+    if st != OK:
+        _raise(st, "int4vh_stream_read")
+    return out

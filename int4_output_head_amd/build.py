@@ -7,7 +7,7 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("int4vh.hip", "requant.hip", "context_copy.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("int4vh.hip", "requant.hip", "context_copy.hip", "stream_probe.hip")]
 OUT = os.path.join(HERE, "libint4vh.so")
 INCLUDE = os.path.join(ROOT, "include")
 

@@ -71,6 +71,10 @@ CONFIGS = {
                        "full-vocab wide verify V=151936 H=5120 T=16"),
     "batch": Config("batch", 64, 4, 151936, 5120, 0.0, "geometric", 0.4, 5,
                     "batch verify 64 requests x T=4 V=151936 H=5120"),
+    # one GPU's share of the full-vocabulary head split by vocabulary rows
+    # over 8 GPUs (151936 / 8 = 18992 rows), at the wide verify block
+    "shard_t16": Config("shard_t16", 1, 16, 18992, 5120, 0.05, "bernoulli_all", 0.9, 20,
+                        "vocabulary shard of 8 (V=18992) wide verify H=5120 T=16"),
 }
 
 

@@ -54,7 +54,8 @@ def test_header_declares_expected_api():
               "context_copy_propose", "context_copy_propose_timed",
               "requant_lm_head_int4_amax",
               "requant_lm_head_int4_scales", "requant_lm_head_int4_pack",
-              "requant_lm_head_int4_pack_timed", "requant_lm_head_int4"):
+              "requant_lm_head_int4_pack_timed", "requant_lm_head_int4",
+              "verify_lm_head_int4_batch_noalloc", "int4vh_stream_read"):
         assert n in names, n
 
 

@@ -15,6 +15,14 @@ Parity rule (from the logit tolerance tol[r] = 2e-3 * max_v |oracle logit|):
     uniforms and draft probabilities (binary32 product and compare), and the
     oracle's unless the first differing decision is a near tie
     (|u q - p_oracle| within the p_draft bound).
+
+The epilogue's own arithmetic is checked much tighter, separately from the
+logit error: the oracle's formulas (top-k probability, log-sum-exp, whole-
+vocabulary probability) are evaluated in binary64 on the GPU's own logits
+(the greedy path's full logits, which the sampled path reproduces bit for
+bit), and the GPU's binary32 results must agree within a bound built from
+binary32 rounding: about 1e-5 relative, growing with |logit| / tau (each
+exponent argument is rounded once, u |argument|).
 """
 import math
 import sys
@@ -75,13 +83,61 @@ def make_drafts(lg, R, T, k, seed):
 
 def run(vh, inp, d, q, u, R, T, V, H, k, tau):
     T1 = T - 1
-    out = vh.verify_sampled(dev(inp["hidden"], torch.float16).reshape(R, T, H), dev(inp["packed"]),
-                            dev(inp["scales"], torch.float16),
-                            dev(d) if T1 else None, dev(q) if T1 else None, dev(u) if T1 else None,
+    x = dev(inp["hidden"], torch.float16).reshape(R, T, H)
+    w = dev(inp["packed"])
+    s = dev(inp["scales"], torch.float16)
+    out = vh.verify_sampled(x, w, s, dev(d) if T1 else None, dev(q) if T1 else None, dev(u) if T1 else None,
                             top_k=k, temperature=tau, want_lse=True)
     torch.cuda.synchronize()
     names = ("logits_max", "argmax_ids", "topk_ids", "topk_logits", "p_draft", "n_accepted", "lse")
-    return {n: (None if t is None else t.cpu().numpy()) for n, t in zip(names, out)}
+    g = {n: (None if t is None else t.cpu().numpy()) for n, t in zip(names, out)}
+    # the GPU's own logits: the greedy call with every logit written
+    dd = dev(np.zeros((R, T1), np.int32)) if T1 else None
+    g["logits"] = vh.verify_batch(x, w, s, dd, logits=True)[3].cpu().numpy()
+    return g
+
+
+U32 = 2.0 ** -24    # unit roundoff of binary32
+
+
+def check_own_logits(g, d, R, T, k, tau):
+    """The epilogue's arithmetic on the GPU's own logits (binary64 formulas of
+    the oracle), with binary32 rounding bounds.  Returns the largest relative
+    errors seen."""
+    lg = g["logits"].astype(np.float64)
+    M, V = lg.shape
+    st = dict(own_p_rel=0.0, own_lse_abs=0.0)
+    if k > 0:
+        # the top-k ids and logits are the GPU's own logits, bit for bit
+        for r in range(M):
+            assert np.array_equal(g["topk_logits"][r], g["logits"][r, g["topk_ids"][r]]), r
+            assert np.array_equal(g["topk_ids"][r], sm.topk_rows(g["logits"][r:r + 1], k)[0][0]), r
+    # log-sum-exp over the whole vocabulary
+    lse_ref = sm.lse_rows(g["logits"], tau)
+    zmax = np.abs(lg).max(axis=1) / tau
+    bound_lse = 1e-6 + 8 * U32 * (zmax + np.log(V) + 1)
+    err = np.abs(g["lse"].astype(np.float64) - lse_ref)
+    assert np.all(err <= bound_lse), (err, bound_lse)
+    st["own_lse_abs"] = float(err.max())
+    if T == 1:
+        return st
+    for i in range(R):
+        for t in range(T - 1):
+            r = i * T + t
+            pg = float(g["p_draft"][i, t])
+            if k > 0:
+                pe = sm.draft_prob(g["topk_ids"][r], g["topk_logits"][r], int(d[i, t]), tau)
+                vals = g["topk_logits"][r].astype(np.float64)
+                spread = (vals[0] - vals[-1]) / tau
+                rel = 1e-5 + 8 * U32 * 2 * spread
+            else:
+                pe = sm.full_softmax_prob(g["logits"][r], lse_ref[r], int(d[i, t]), tau)
+                ld = abs(lg[r, d[i, t]]) / tau if 0 <= d[i, t] < V else 0.0
+                rel = 1e-5 + bound_lse[r] + 8 * U32 * ld
+            assert abs(pg - pe) <= rel * pe + 1e-35, (i, t, pg, pe, rel)
+            if pe > 0:
+                st["own_p_rel"] = max(st["own_p_rel"], abs(pg - pe) / pe)
+    return st
 
 
 def check_lse(g, o, lg, tau):
@@ -155,7 +211,8 @@ def check(g, o, lg, d, q, u, R, T, k, tau):
 @pytest.mark.parametrize("R,T,V,H,k,tau", [(1, 4, 300, 64, 8, 1.0), (1, 16, 5000, 512, 16, 0.7),
                                            (2, 8, 4097, 256, 5, 1.3), (4, 4, 999, 96, 16, 1.0),
                                            (1, 1, 8192, 5120, 8, 1.0), (3, 5, 2000, 160, 1, 1.0),
-                                           (16, 1, 700, 128, 12, 2.0)])
+                                           (16, 1, 700, 128, 12, 2.0), (1, 16, 5000, 512, 16, 0.3),
+                                           (2, 8, 4097, 256, 8, 2.0), (1, 16, 20000, 1024, 16, 1.3)])
 def test_sampled_parity(vh, oracle_mod, R, T, V, H, k, tau):
     say(f"sampled R={R} T={T} V={V} H={H} k={k} tau={tau}")
     inp = synth.uniform_inputs(R * T, V, H, seed=R * 31 + T + V + H + k)
@@ -165,6 +222,7 @@ def test_sampled_parity(vh, oracle_mod, R, T, V, H, k, tau):
     g = run(vh, inp, d, q, u, R, T, V, H, k, tau)
     st = check(g, o, lg, d, q, u, R, T, k, tau)
     st["lse_max_err"] = check_lse(g, o, lg, tau)
+    st.update(check_own_logits(g, d, R, T, k, tau))
     say(f"stats {st}")
 
 
@@ -201,7 +259,8 @@ def check_full_softmax(g, o, lg, d, q, u, R, T, tau):
 
 
 @pytest.mark.parametrize("R,T,V,H,tau", [(1, 16, 5000, 512, 1.0), (2, 8, 4097, 256, 0.3),
-                                         (4, 4, 999, 96, 2.0), (1, 8, 151936, 5120, 1.0)])
+                                         (4, 4, 999, 96, 2.0), (1, 8, 151936, 5120, 1.0),
+                                         (1, 16, 20000, 1024, 0.7), (2, 4, 3000, 256, 1.3)])
 def test_full_softmax_parity(vh, oracle_mod, R, T, V, H, tau):
     """Sampling over the whole vocabulary (top_k = 0): the fused online
     log-sum-exp and the draft's probability against the oracle."""
@@ -221,7 +280,8 @@ def test_full_softmax_parity(vh, oracle_mod, R, T, V, H, tau):
     g = run(vh, inp, d, q, u, R, T, V, H, 0, tau)
     assert np.all(g["p_draft"][:, -1] == 0.0)
     rel = check_full_softmax(g, o, lg, d, q, u, R, T, tau)
-    say(f"full softmax max relative error of p: {rel:.2e}")
+    own = check_own_logits(g, d, R, T, 0, tau)
+    say(f"full softmax max relative error of p: {rel:.2e}; on the GPU's own logits {own}")
 
 
 def test_sampled_full_vocab_t16(vh, oracle_mod):
@@ -239,6 +299,7 @@ def test_sampled_full_vocab_t16(vh, oracle_mod):
              topk_logits=vals, p_draft=p, n_accepted=n)
     g = run(vh, inp, d, q, u, 1, 16, cfg.V, cfg.H, 16, 1.0)
     st = check(g, o, lg, d, q, u, 1, 16, 16, 1.0)
+    st.update(check_own_logits(g, d, 1, 16, 16, 1.0))
     say(f"full-vocab T=16 stats {st}")
 
 
@@ -279,6 +340,7 @@ def test_sampled_monotone_logits(vh, oracle_mod, k, H):
     o = sm.verify_sampled(x, packed, inp["scales"], d, q, u, R, T, V, H, k, 1.0)
     g = run(vh, inp, d, q, u, R, T, V, H, k, 1.0)
     st = check(g, o, lg, d, q, u, R, T, k, 1.0)
+    st.update(check_own_logits(g, d, R, T, k, 1.0))
     say(f"monotone stats {st}")
 
 

@@ -140,6 +140,18 @@ def test_brute_force_exact_rational(oracle_mod, seed, M, V, H):
         order = sorted(range(V), key=lambda v: (-ex[r][v], v))
         if V > 1 and ex[r][order[0]] - ex[r][order[1]] > 2 * max(bounds):
             assert idx[r] == order[0]
+        # the tolerance inputs: amax is the largest |logit| and gap the best
+        # minus the second-best logit of another index, each within the
+        # summation bounds of the exact values (gap: two logits' bounds plus
+        # the binary32 rounding of the subtraction)
+        b = max(bounds)
+        amax_exact = max(abs(e) for e in ex[r])
+        assert abs(Fraction(float(amax[r])) - amax_exact) <= b
+        if V > 1:
+            gap_exact = ex[r][order[0]] - ex[r][order[1]]
+            assert abs(Fraction(float(gap[r])) - gap_exact) <= 2 * b + abs(gap_exact) * u + u * b
+        else:
+            assert np.isinf(gap[r])
 
 
 @pytest.mark.parametrize("seed,M,V,H", [(0, 4, 300, 128), (1, 16, 257, 512), (2, 3, 64, 5120)])
@@ -172,6 +184,34 @@ def test_int_exact_ties_lowest_index(oracle_mod):
     lg2 = oracle_mod.logits(d["hidden"], synth.pack_int4(q2), d["scales"], M, V, H)
     idx, _, gap, _ = oracle_mod.argmax_rows(lg2)
     assert idx[0] == 0 and gap[0] == 0.0
+
+
+def test_argmax_rows_hand_cases(oracle_mod, hand):
+    """argmax, max, gap and amax of hand-written logit rows: the largest
+    |logit| coming from a negative logit, all-negative rows, ties at the
+    maximum (gap 0), nonzero gaps, V = 1 (gap +inf) and signed zeros."""
+    for c in hand["argmax_rows"]["rows"]:
+        lg = np.array([c["logits"]], np.float32)
+        idx, mx, gap, amax = oracle_mod.argmax_rows(lg)
+        want_gap = np.inf if c["gap"] == "inf" else c["gap"]
+        assert (int(idx[0]), float(mx[0]), float(gap[0]), float(amax[0])) == \
+            (c["argmax"], c["max"], want_gap, c["amax"]), c["_why"]
+
+
+def test_verify_small_hand_case(oracle_mod, hand):
+    """The whole verify step on a 3 x 4 x 2 case worked out by hand."""
+    c = hand["verify_small"]
+    V, H, R, T = c["V"], c["H"], c["R"], c["T"]
+    x = np.array(c["hidden"], np.uint16).reshape(R * T, H)
+    out = oracle_mod.verify(x, np.array(c["bytes"], np.uint8).reshape(V, H // 2),
+                            np.array(c["scales"], np.uint16), np.array(c["drafts"], np.int32), R, T, V, H,
+                            want_logits=True)
+    assert out["logits"].tolist() == c["logits"]
+    assert out["argmax_ids"].tolist() == c["argmax"]
+    assert out["logits_max"].tolist() == c["max"]
+    assert out["gap"].tolist() == c["gap"]
+    assert out["amax"].tolist() == c["amax"]
+    assert int(out["n_accepted"][0]) == c["n_accepted"]
 
 
 # ------------------------------------------------------------------ invariants
