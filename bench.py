@@ -325,6 +325,88 @@ def bench_stream(args):
     print(json.dumps(result), flush=True)
 
 
+SWEEP_ROWS = (1, 2, 4, 8, 16, 17, 24, 32, 48, 64, 96, 128, 192, 256, 512)
+
+
+def bench_sweep(args):
+    """Cost of one verify call against the number of rows M it verifies (M
+    requests of one position each: the weight-stream path up to 16 rows, the
+    matrix-core path beyond), full-vocabulary head V=151936, H=5120, two head
+    copies rotated.  Per M: the whole call in a HIP graph of 20 calls
+    (replayed after an untimed warm-up) and the main kernel alone (HIP events,
+    eager).  The leg's value is the verified rows/s at M = 32."""
+    import torch
+    from int4_output_head_amd import binding, synth
+
+    dev = torch.device("cuda:0")
+    binding.load_library()
+    cfg = synth.CONFIGS["full_t16"]
+    head = synth.make_head(cfg)
+    w0 = torch.from_numpy(head["packed"]).to(dev)
+    ws = [w0, w0.clone()]
+    s = torch.from_numpy(head["scales"]).view(torch.float16).to(dev)
+    rows_max = max(SWEEP_ROWS)
+    rng = np.random.default_rng(0)
+    x_all = torch.from_numpy(synth.f16_bits(rng.standard_normal((rows_max, cfg.H)))).view(torch.float16).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    curve = []
+    for M in SWEEP_ROWS:
+        x = x_all[:M].reshape(M, 1, cfg.H).contiguous()
+        work = binding.Workspace(binding.workspace_bytes(M, 1, cfg.V, cfg.H), dev)
+        for i in range(10):
+            binding.verify_batch(x, ws[i % 2], s, None, workspace=work)
+        torch.cuda.synchronize()
+        n_ev = 40
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+        for i in range(n_ev):
+            binding.verify_batch(x, ws[i % 2], s, None, workspace=work, events=ev[i])
+        torch.cuda.synchronize()
+        main_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            binding.verify_batch(x, ws[0], s, None, workspace=work)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(20):
+                    binding.verify_batch(x, ws[i % 2], s, None, workspace=work)
+        torch.cuda.synchronize()
+        t_w = time.time()
+        while time.time() - t_w < 0.2:
+            g.replay()
+            torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        g0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        us = g0.elapsed_time(g1) * 1e3 / (reps * 20)
+        rec = dict(M=M, us_per_call=round(us, 2), main_kernel_us=round(main_us, 2),
+                   weight_GB_s=round(cfg.weight_bytes / (us * 1e-6) / 1e9, 1),
+                   rows_per_s=round(M / (us * 1e-6), 1),
+                   int8_TOPs_algorithmic=round(2.0 * M * cfg.V * cfg.H / (main_us * 1e-6) / 1e12, 1))
+        curve.append(rec)
+        log(f"sweep {rec}")
+        del work, g
+    at = {r["M"]: r for r in curve}
+    result = {
+        "metric": "int4 lm_head verify: verified rows/s against rows per call (full vocabulary)",
+        "value": at[32]["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": 100, "warmup": 10,
+        "ms_per_step": round(at[32]["us_per_call"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
+        "config": {"workload": "verify calls of M rows, V=151936 H=5120, M in " + str(list(SWEEP_ROWS)),
+                   "timing": "HIP graph of 20 calls replayed 5x per M; main kernel by HIP events"},
+        "curve": curve,
+        "ratio_32_to_16_rows": round(at[32]["us_per_call"] / at[16]["us_per_call"], 3),
+        "cpu_baseline": None,
+        "cpu_baseline_note": "the oracle's cost grows linearly with M; see the full_t16 and batch legs",
+    }
+    print(json.dumps(result), flush=True)
+
+
 def bench_context_copy(args):
     """The context-copy drafter on the workload of the wide verify block: a
     25,000-token synthetic prompt per request, a 16-token key whose tail
@@ -431,6 +513,9 @@ def main():
         return
     if args.config == "stream":
         bench_stream(args)
+        return
+    if args.config == "sweep":
+        bench_sweep(args)
         return
 
     import torch

@@ -124,12 +124,12 @@ int verify_lm_head_int4(const void *hidden, const uint8_t *packed_w, const void 
 
 /* R independent requests of T positions each, sharing one head.  Rows of
  * request i are hidden[i*T .. i*T+T-1]; its drafts are draft_ids[i*(T-1) ..].
- * Per-request acceptance goes to n_accepted[i].  Up to 16 rows the call runs
- * the weight-stream kernels; beyond, up to INT4VH_MAX_ROWS rows, it runs a
- * GEMM on the int8 matrix cores whose workspace grows with R*T
- * (verify_lm_head_int4_workspace_bytes).  The batch mode of the HyperQwen
- * README, "The numbers behind that", serves 64 requests at once: 64 x 4 =
- * 256 rows.  Results are identical either way. */
+ * Per-request acceptance goes to n_accepted[i].  Up to 64 rows the call runs
+ * the weight-stream kernels (in token groups of 16 beyond 16 rows); beyond,
+ * up to INT4VH_MAX_ROWS rows, it runs a GEMM on the int8 matrix cores.  The
+ * workspace grows with R*T (verify_lm_head_int4_workspace_bytes).  The batch
+ * mode of the HyperQwen README, "The numbers behind that", serves 64 requests
+ * at once: 64 x 4 = 256 rows.  Results are identical either way. */
 int verify_lm_head_int4_batch(const void *hidden, const uint8_t *packed_w, const void *scales,
                               const int32_t *draft_ids, int R, int T, int V, int H,
                               float *logits_max, int32_t *argmax_ids, int32_t *n_accepted,

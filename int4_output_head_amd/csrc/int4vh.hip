@@ -1,8 +1,9 @@
 // int4vh.hip -- int4 lm_head speculative verification for MI355X (gfx950).
 //
 // One call computes, for a verify block of M <= 16 rows of final hidden
-// states, every logit of a calibrated int4 head, the greedy argmax of each
-// row and the accepted-prefix length of each request.  The head is the
+// states (up to 64 in token groups of 16, below), every logit of a
+// calibrated int4 head, the greedy argmax of each row and the
+// accepted-prefix length of each request.  The head is the
 // requantised lm_head of "Qwen3.8-27B on a Single RTX 3090: How Calibrated
 // Quantization and Speculative Decoding Hit 1,000 tok/s", Technical Insight
 // (values in [-7, 7], one scale per hidden channel); the greedy compare of a
@@ -39,6 +40,16 @@
 //      workgroup to finish (two-level atomic ticket) merges the per-workgroup
 //      winners, writes the outputs, counts accepted drafts and resets the
 //      tickets.
+//
+//  Blocks of 17 to 64 rows run the same two kernels in token groups of 16:
+//  the registers of a workgroup hold the activation codes of 16 rows (all 24
+//  bits of 16 rows x 5120 channels fill half the register file), so each
+//  group gets its own workgroups, one per tile set, and the workgroups of a
+//  set (one per group, 8 blockIdx apart: the same XCD) walk the same tiles
+//  at the same time, so a tile comes from HBM once and from that XCD's L2
+//  for the others.  Per-tile time is bound by the latency of the three-tile
+//  ring, so the call costs about 46 us more per group; above 64 rows the
+//  matrix-core batch kernels below are faster.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -47,6 +58,7 @@
 
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 #include <string>
 
 #include "int4vh.h"
@@ -94,7 +106,8 @@ constexpr int kThreads = 64 * kWaves;     // 512
 constexpr int kTileRows = 16;             // vocabulary rows per tile (MFMA N)
 constexpr int kUnitH = 128;               // hidden channels per unit (16 rows x 64 B = 1 KB)
 constexpr int kMaxUnitsPerWave = 8;       // 8 waves x 8 units x 128 = 8192 channels
-constexpr int kMaxRows = 16;              // rows per launch (MFMA M)
+constexpr int kMaxRows = 16;              // rows per token group (MFMA M)
+constexpr int kMaxGroups = 4;             // token groups per launch: up to 64 rows in the weight stream
 constexpr int kCodeMax = 8355711;         // |code| bound: all three limbs stay in int8
 constexpr int kMaxGrid = 1024;            // partial slots in the workspace
 constexpr int kStageThreads = 512;        // threads of stage_kernel (one 16-channel chunk each)
@@ -289,6 +302,11 @@ struct Args {
     int n_units;              // ceil(H / 128)
     int n_tiles;              // ceil(V / 16)
     unsigned long long w_bytes;
+    // Blocks of more than 16 rows: groups of 16 rows, each with its own
+    // workgroups (one per tile set) and activation fragments
+    int n_groups;             // ceil(M / 16); 1 up to 16 rows
+    int n_sets;               // workgroups per group; grid = n_groups * n_sets
+    size_t group_words;       // 16-byte fragment words per group
 };
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t b)
@@ -652,10 +670,13 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
 {
     constexpr int kGroups = Slots<kP>::kGroups;
     __shared__ float s_red[kStageThreads / 64];
-    const int tau = blockIdx.x;
+    // slot tau of token group blockIdx.x / kP (one group when kP < 16)
+    const int tau = (int)blockIdx.x % kP;
+    const int tok = (int)blockIdx.x;
+    u32x4 *frag_out = a.frag_out + (size_t)(tok / kP) * a.group_words;
     const int H = a.H;
-    const bool live = tau < a.M;
-    const uint16_t *hrow = a.hidden + (size_t)(live ? tau : 0) * H;
+    const bool live = tok < a.M;
+    const uint16_t *hrow = a.hidden + (size_t)(live ? tok : 0) * H;
     const int n_chunks = kWaves * kUnits * 8;              // 16-channel chunks in the padded row
     constexpr int kIter = (kWaves * kMaxUnitsPerWave * 8 + kStageThreads - 1) / kStageThreads;
 
@@ -686,7 +707,7 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
         am = fmaxf(am, s_red[w]);
     const int e = code_exponent(am);
     if (threadIdx.x == 0)
-        a.exps[tau] = e;
+        a.exps[tok] = e;
 
 #pragma unroll
     for (int it = 0; it < kIter; ++it) {
@@ -706,14 +727,15 @@ __global__ void __launch_bounds__(kStageThreads) stage_kernel(Args a)
                 u32x4 word = {0u, 0u, 0u, 0u};
                 if (limb < 3)
                     word = u32x4{limbw[limb][0], limbw[limb][1], limbw[limb][2], limbw[limb][3]};
-                a.frag_out[frag_index<kP, kUnits>(wave, i, t, g, grp * 16 + n16)] = word;
+                frag_out[frag_index<kP, kUnits>(wave, i, t, g, grp * 16 + n16)] = word;
             }
         }
     }
 }
 
 // ---------------------------------------------------------------- verify_kernel
-template <int kP, int kUnits, int kRing, bool kLogits, int kTopK, bool kLse, bool kFused>
+template <int kP, int kUnits, int kRing, bool kLogits, int kTopK, bool kLse, bool kFused,
+          int kAux = INT4VH_WEIGHT_AUX>
 __global__ void __launch_bounds__(kThreads)
 verify_kernel(Args a)
 {
@@ -731,6 +753,8 @@ verify_kernel(Args a)
         int draft[kMaxRows];
         int accept[kMaxRows];
         int last;
+        int arg_g[kMaxGroups * kMaxRows];     // several token groups: ids of every row
+        int draft_g[kMaxGroups * kMaxRows];   // and the drafts of every request
     };
     // Sampled epilogue: a per-token buffer of candidate keys, sorted into the
     // top-k list 16 at a time -- where the LDS budget leaves room for it
@@ -761,7 +785,17 @@ verify_kernel(Args a)
     const int G = gridDim.x;
     const int b = blockIdx.x;
     const int M = a.M, V = a.V, H = a.H;
-    const int n_my = (a.n_tiles - b + G - 1) / G;
+    // Token groups (more than 16 rows): one workgroup of each group per tile
+    // set, all walking the same tiles.  With whole sets of 8 workgroups the
+    // members of a set are 8 blockIdx apart, so they run on one XCD (blockIdx
+    // b runs on XCD b % 8) at the same time and a tile comes from HBM once,
+    // then from that XCD's L2.
+    const int n_g = a.n_groups, n_sets = a.n_sets;
+    const int tgrp = n_g == 1 ? 0 : (n_sets % 8 == 0 ? (b / 8) % n_g : b / n_sets);
+    const int tset = n_g == 1 ? b : (n_sets % 8 == 0 ? (b % 8) + 8 * (b / (8 * n_g)) : b % n_sets);
+    const int Mg = n_g == 1 ? M : min(kMaxRows, M - kMaxRows * tgrp);   // rows of this group
+    const int pstride = n_g == 1 ? M : kMaxRows;                        // winners per workgroup
+    const int n_my = (a.n_tiles - tset + n_sets - 1) / n_sets;
     const int chunks_per_row = H / 32;                     // 16-byte chunks per weight row
 
     // ---------------- weight stream into the LDS ring
@@ -784,7 +818,7 @@ verify_kernel(Args a)
     // throughout): the compiler then counts the copies in flight exactly and
     // does not wait for all of them before the first use of the fragments.
     auto issue_tile = [&](int k, bool branch_free = false) {
-        const int tile = b + k * G;
+        const int tile = tset + k * n_sets;
         const unsigned long long base = (unsigned long long)tile * tile_bytes;
         uint8_t *dst = s_ring[k % kRing];
         if (!branch_free && base + span_bytes <= a.w_bytes) {   // all of the tile's copies inside the head
@@ -792,20 +826,20 @@ verify_kernel(Args a)
 #pragma unroll
             for (int m = 0; m < kUnits; ++m) {
                 const int jj = min(wave * kUnits + m, a.n_units - 1);
-                copy_to_lds16<INT4VH_WEIGHT_AUX>(src + loff[m], dst + jj * 1024);
+                copy_to_lds16<kAux>(src + loff[m], dst + jj * 1024);
             }
         } else {
 #pragma unroll
             for (int m = 0; m < kUnits; ++m) {
                 const int jj = min(wave * kUnits + m, a.n_units - 1);
                 const unsigned long long off = base + loff[m];
-                copy_to_lds16<INT4VH_WEIGHT_AUX>(a.w + (off < w_last ? off : w_last), dst + jj * 1024);
+                copy_to_lds16<kAux>(a.w + (off < w_last ? off : w_last), dst + jj * 1024);
             }
         }
     };
     // ---------------- activation fragments and step exponents
-    const int rtok = 2 * wave + ((lane >> 4) & 1);         // token reduced by this lane
-    const bool rlane = lane < 32 && rtok < M;
+    const int rtok = 2 * wave + ((lane >> 4) & 1);         // token (of the group) reduced by this lane
+    const bool rlane = lane < 32 && rtok < Mg;
     i32x4 afr[kUnits][2][kGroups];
     int rexp;
     // sampled epilogue: the draft id of the lane's token (loaded ahead of the
@@ -821,7 +855,8 @@ verify_kernel(Args a)
             for (int t = 0; t < 2; ++t)
 #pragma unroll
                 for (int g = 0; g < kGroups; ++g)
-                    afr[i][t][g] = __builtin_bit_cast(i32x4, a.frag[frag_index<kP, kUnits>(wave, i, t, g, lane)]);
+                    afr[i][t][g] = __builtin_bit_cast(
+                        i32x4, a.frag[(size_t)tgrp * a.group_words + frag_index<kP, kUnits>(wave, i, t, g, lane)]);
         // the prologue tiles, unconditional like the first step's (a tile
         // past the head reads clamped bytes into a ring slot that is never
         // used; every copy has landed before the workgroup publishes)
@@ -832,7 +867,7 @@ verify_kernel(Args a)
         // the copies are out (a vector load would make the compiler wait for
         // every copy in flight where it is first used); lanes of tokens >= M
         // never use theirs
-        rexp = load_exp_pair(a.exps + 2 * wave, (lane >> 4) & 1) - 4;   // weights carry a factor 16
+        rexp = load_exp_pair(a.exps + kMaxRows * tgrp + 2 * wave, (lane >> 4) & 1) - 4;   // weights carry a factor 16
     } else {
         // Staging done here for M <= 2 rows.  The scale row and the hidden
         // rows are copied into the last ring slot (unused until the main loop
@@ -1022,7 +1057,7 @@ verify_kernel(Args a)
                 code += __longlong_as_double((long long)s_part[buf][w][rt + kP * j][n16]);
         unsigned long long key = 0ull;
         if (rlane) {
-            const int v = (b + k * G) * kTileRows + n16;
+            const int v = (tset + k * n_sets) * kTileRows + n16;
             const float val = (float)ldexp(code, rexp);   // the one rounding
             if (v < V) {
                 if constexpr (kTopK == 0) {       // (the sampled epilogue's winner is its list's rank 0)
@@ -1041,7 +1076,7 @@ verify_kernel(Args a)
                     }
                 }
                 if (kLogits)
-                    a.logits_out[(size_t)rtok * V + v] = val;
+                    a.logits_out[(size_t)(kMaxRows * tgrp + rtok) * V + v] = val;
             }
         }
         if (kCBuf && k == 0) {
@@ -1197,7 +1232,7 @@ verify_kernel(Args a)
     // store has landed before the ticket is incremented, and the last
     // workgroup reads them with agent-scope atomic loads.
     if (kTopK == 0 && rlane && n16 == 0)           // (the sampled epilogue's winners are in its lists)
-        __hip_atomic_store(&a.part[(size_t)b * M + rtok], pack_pair(bv, bi), __ATOMIC_RELAXED,
+        __hip_atomic_store(&a.part[(size_t)b * pstride + rtok], pack_pair(bv, bi), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
@@ -1208,7 +1243,7 @@ verify_kernel(Args a)
         // workgroup of each group of 16 takes the top-level ticket.
         if (threadIdx.x == 0) {
             bool last;
-            if (a.n_tiles >= 8 * G) {
+            if (a.n_tiles >= 8 * n_sets) {
                 last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                        (uint32_t)(G - 1);
             } else {
@@ -1275,6 +1310,65 @@ verify_kernel(Args a)
         __syncthreads();
         if (!s_last)
             return;
+    }
+
+    // ---------------- last workgroup, several token groups (greedy only)
+    // Four threads per row m: they load the winners of the n_sets workgroups
+    // of group m / 16 (every load issued before any is used), reduce them,
+    // and the rows' ids and the drafts go to LDS for the acceptance count.
+    if (kTopK == 0 && n_g > 1) {
+        constexpr int kPerThread = kMaxGrid / kMaxGroups / 4;    // winners per thread, at most
+        const int m = (int)threadIdx.x >> 2, sub = (int)threadIdx.x & 3;
+        const int mm = m < M ? m : M - 1;
+        const int gm = mm / kMaxRows, l = mm % kMaxRows;
+        float v0 = -__builtin_huge_valf();
+        int i0 = 0x7FFFFFFF;
+        uint64_t p[kPerThread];
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int js = sub + 4 * j;
+            const int jj = js < n_sets ? js : n_sets - 1;   // repeats are harmless for a maximum
+            const int bb = n_sets % 8 == 0 ? 8 * (n_g * (jj / 8) + gm) + jj % 8 : gm * n_sets + jj;
+            p[j] = __hip_atomic_load(&a.part[(size_t)bb * kMaxRows + l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const float pv = __uint_as_float((uint32_t)p[j]);
+            const int pi = (int)(uint32_t)(p[j] >> 32);
+            if (better(pv, pi, v0, i0)) {
+                v0 = pv;
+                i0 = pi;
+            }
+        }
+#pragma unroll
+        for (int off = 1; off <= 2; off <<= 1) {
+            const float ov = __shfl_xor(v0, off);
+            const int oi = __shfl_xor(i0, off);
+            if (better(ov, oi, v0, i0)) {
+                v0 = ov;
+                i0 = oi;
+            }
+        }
+        const int n_draft = a.R * (a.T - 1);
+        if (sub == 0 && m < M) {
+            const int id = a.vmap ? a.vmap[i0] : i0;    // row -> token id
+            a.logits_max[m] = v0;
+            a.argmax[m] = id;
+            mg.arg_g[m] = id;
+        }
+        if ((int)threadIdx.x < n_draft)
+            mg.draft_g[threadIdx.x] = a.draft[threadIdx.x];
+        __syncthreads();
+        for (int i = threadIdx.x; i < a.R; i += kThreads) {
+            const int T = a.T;
+            int n = 0;
+            while (n < T - 1 && mg.arg_g[i * T + n] == mg.draft_g[i * (T - 1) + n])
+                ++n;
+            a.n_acc[i] = n;
+        }
+        if (threadIdx.x == 0)
+            __hip_atomic_store(a.ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return;
     }
 
     // ---------------- last workgroup: merge, write, accept, reset
@@ -1444,7 +1538,7 @@ verify_kernel(Args a)
 
 // ================================================================ batch path
 //
-// Blocks of more than 16 rows (up to 4096: many requests sharing one head).
+// Blocks of more than 64 rows (up to 4096: many requests sharing one head).
 // The contraction is then a GEMM of (token, limb) rows against the head,
 // 3M x H times H x V, on the same int8 MFMA and with the same numerics as the
 // single-block kernels (identical codes, exact integer sums, one
@@ -1484,9 +1578,9 @@ verify_kernel(Args a)
 
 constexpr int kRWaves = 8;                              // waves per workgroup
 constexpr int kRThreads = 64 * kRWaves;
-constexpr int kRTbPerWave = 8 / kRWaves;                // 16-token blocks per wave
-constexpr int kRTbPerTile = kRTbPerWave * kRWaves;      // 16-token blocks per work item
-constexpr int kRTokTile = 16 * kRTbPerTile;             // tokens per work item
+constexpr int kRTbPerWave = 8 / kRWaves;                // 16-token blocks per wave (128-token kernel)
+constexpr int kRTbPerTile = kRTbPerWave * kRWaves;      // 16-token blocks per work item (128-token kernel)
+constexpr int kRTokTile = 16 * kRTbPerTile;             // tokens per work item (128-token kernel)
 constexpr int kRVocTile = 128;                          // vocabulary rows per work item
 constexpr int kRVBlocks = kRVocTile / 16;               // MFMA column blocks per wave
 constexpr int kRStepH = 128;                            // hidden channels per K step
@@ -1511,13 +1605,13 @@ struct RArgs {
     unsigned long long *keys; // [M] per-token winner keys, zero between calls
     uint32_t *ticket;
     uint32_t *group_ticket;   // [64][kTicketStride] per-group tickets (word 0), zero between calls
-    int32_t *exps;            // [n_mt * 128] step exponents
+    int32_t *exps;            // [n_mt * token tile] step exponents
     const u32x4 *frag;        // activation fragments
     u32x4 *frag_out;
     int R, T, M, V, H;
     int n_steps;              // K steps of 128 channels, rounded up to even
     int n_tb;                 // 16-token blocks that hold real rows: ceil(M / 16)
-    int n_mt;                 // 128-token tiles: ceil(M / 128)
+    int n_mt;                 // token tiles of 32, 64 or 128 tokens: ceil(M / tile)
     int n_items;              // n_mt * ceil(V / 128)
     unsigned long long w_bytes;
 };
@@ -1964,6 +2058,31 @@ Pair make_pair()
     return Pair{stage_kernel<kP, kUnits>, verify_kernel<kP, kUnits, kRing, kLogits, kTopK, kLse, false>};
 }
 
+// Token groups of 16 rows sharing the tile stream: the weight copies use
+// the normal cache policy, so that the workgroups of a tile set that ask for
+// a tile after the first find it in their XCD's L2.
+template <int kUnits, bool kLogits>
+Pair make_grouped()
+{
+    constexpr int kRing = kUnits <= 5 ? 3 : 2;
+    return Pair{stage_kernel<16, kUnits>, verify_kernel<16, kUnits, kRing, kLogits, 0, false, false, 0>};
+}
+
+template <bool kLogits>
+Pair pick_grouped(int units)
+{
+    switch (units) {
+    case 1: return make_grouped<1, kLogits>();
+    case 2: return make_grouped<2, kLogits>();
+    case 3: return make_grouped<3, kLogits>();
+    case 4: return make_grouped<4, kLogits>();
+    case 5: return make_grouped<5, kLogits>();
+    case 6: return make_grouped<6, kLogits>();
+    case 7: return make_grouped<7, kLogits>();
+    default: return make_grouped<8, kLogits>();
+    }
+}
+
 // One launch, staging inside the verify kernel (up to 2 rows).
 template <int kUnits, bool kLogits>
 Pair make_fused()
@@ -2044,6 +2163,10 @@ int rows_steps(int H)
     return (n + 1) & ~1;
 }
 
+// Rows of the largest call the weight-stream kernels take (token groups of
+// 16 sharing the tile stream); larger calls run the matrix-core batch path.
+constexpr int kStreamMaxRows = kMaxRows * kMaxGroups;
+
 size_t workspace_need(int R, int T, int V, int H)
 {
     if (R < 1 || T < 1 || T > INT4VH_MAX_T || V < 1 || H < 32 || (H % 32) != 0)
@@ -2053,8 +2176,10 @@ size_t workspace_need(int R, int T, int V, int H)
         return 0;
     if (M <= kMaxRows)
         return kWsBytes;
+    if (M <= kStreamMaxRows)   // one fragment area per token group
+        return kWsFrag + (size_t)((M + kMaxRows - 1) / kMaxRows) * kFragBytes;
     const size_t n_mt = (size_t)((M + kRTokTile - 1) / kRTokTile);
-    return kWsFrag + n_mt * kRTbPerTile * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
+    return kWsFrag + n_mt * (size_t)kRTbPerTile * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
 }
 
 // Every argument check except the workspace's (no GPU call).
@@ -2193,7 +2318,7 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
 
     char *wsb = static_cast<char *>(ws);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    if (R * T > kMaxRows)
+    if (R * T > kStreamMaxRows)
         return launch_rows(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lout, vmap,
                            wsb, dev, s, ev0, ev1);
     Args a;
@@ -2238,17 +2363,36 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     int grid = cu_count(dev);
     if (grid > kMaxGrid)
         grid = kMaxGrid;
-    if (grid > a.n_tiles)
-        grid = a.n_tiles;
-    if (smp && grid > kSampledMaxGrid)
-        grid = kSampledMaxGrid;
+    // more than 16 rows: token groups of 16, one workgroup of each group per
+    // tile set (whole sets of 8 when there are 8 or more, so a set shares an
+    // XCD; at most 128 sets, the final merge's capacity)
+    a.n_groups = (a.M + kMaxRows - 1) / kMaxRows;
+    a.group_words = kFragBytes / sizeof(u32x4);
+    if (a.n_groups > 1) {
+        int sets = grid / a.n_groups;
+        if (sets > kMaxGrid / kMaxGroups)
+            sets = kMaxGrid / kMaxGroups;
+        if (sets > a.n_tiles)
+            sets = a.n_tiles;
+        if (sets >= 8)
+            sets -= sets % 8;
+        a.n_sets = sets;
+        grid = sets * a.n_groups;
+    } else {
+        if (grid > a.n_tiles)
+            grid = a.n_tiles;
+        if (smp && grid > kSampledMaxGrid)
+            grid = kSampledMaxGrid;
+        a.n_sets = grid;
+    }
     int kp = 16;
-    const bool fused = !smp && fused_staging(a.M, units);
-    const Pair fn = fused ? (lout ? pick_fused<true>(units) : pick_fused<false>(units))
-                          : pick_kernels(a.M, units, lout != nullptr, smp != nullptr, smp ? smp->top_k : 0,
-                                         smp && (smp->top_k == 0 || smp->lse != nullptr), &kp);
+    const bool fused = !smp && a.n_groups == 1 && fused_staging(a.M, units);
+    const Pair fn = fused            ? (lout ? pick_fused<true>(units) : pick_fused<false>(units))
+                    : a.n_groups > 1 ? (lout ? pick_grouped<true>(units) : pick_grouped<false>(units))
+                                     : pick_kernels(a.M, units, lout != nullptr, smp != nullptr, smp ? smp->top_k : 0,
+                                                    smp && (smp->top_k == 0 || smp->lse != nullptr), &kp);
     if (fn.stage) {
-        hipLaunchKernelGGL(fn.stage, dim3(kp), dim3(kStageThreads), 0, s, a);
+        hipLaunchKernelGGL(fn.stage, dim3(kp * a.n_groups), dim3(kStageThreads), 0, s, a);
         e = hipGetLastError();
         if (e != hipSuccess)
             return hip_fail(e, "stage kernel launch");

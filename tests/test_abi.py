@@ -135,16 +135,22 @@ def test_batch_workspace_bytes(lib):
     wb = lib.verify_lm_head_int4_workspace_bytes
     assert wb(4097, 1, 10, 64) == 0 and wb(257, 16, 10, 64) == 0
     small = wb(1, 16, 151936, 5120)
-    # up to 16 rows: the single-block layout; beyond: activation fragments
-    # of 128-row tiles, 3 bytes per row and (padded) channel
+    # up to 16 rows: the single-block layout; 17-64 rows: one activation
+    # fragment area per group of 16 rows (the weight-stream kernels); beyond:
+    # activation fragments of 128-row tiles, 3 bytes per row and (padded)
+    # channel (the matrix-core batch kernels)
     assert wb(4, 4, 151936, 5120) == small
     big = wb(64, 4, 151936, 5120)
     assert big > small and big % 256 == 0
     assert wb(256, 16, 10, 64) > 0
-    per_tile = (wb(256, 1, 10, 5120) - wb(128, 1, 10, 5120))
+    per_tile = (wb(384, 1, 10, 5120) - wb(256, 1, 10, 5120))
     assert per_tile == 128 * 5120 * 3
+    assert wb(65, 1, 10, 5120) == wb(128, 1, 10, 5120)
     assert wb(129, 1, 10, 5120) == wb(256, 1, 10, 5120)
-    assert wb(17, 1, 10, 5120) == wb(128, 1, 10, 5120)
+    assert wb(17, 1, 10, 5120) == wb(32, 1, 10, 5120)
+    group = wb(48, 1, 10, 5120) - wb(32, 1, 10, 5120)
+    assert group > 0 and group % 256 == 0
+    assert wb(64, 1, 10, 5120) - wb(17, 1, 10, 5120) == 2 * group
 
 
 def test_workspace_init_and_check_weights_validation(lib):

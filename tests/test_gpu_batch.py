@@ -127,6 +127,27 @@ def test_batch_rows_match_single_block_path(vh, orc):
         assert one["n_accepted"][0] == big["n_accepted"][i]
 
 
+def test_token_tiles_bit_identical(vh, orc):
+    """The batch path picks a token tile of 32, 64 or 128 rows from the call
+    size; the same 24 rows inside calls of 24, 48 and 160 rows (one of each
+    tile) give bit-identical logits, maxima and ids, and match the oracle."""
+    V, H = 3001, 1280
+    d = synth.uniform_inputs(160, V, H, seed=31, heavy_frac=0.05)
+    x = d["hidden"].reshape(160, H)
+    outs = []
+    for M in (24, 48, 160):
+        say(f"token tile check M={M}")
+        g = run_gpu(vh, np.ascontiguousarray(x[:M]), d["packed"], d["scales"], np.zeros((M, 0), np.int32), M, 1)
+        outs.append(g)
+    for g in outs[1:]:
+        assert np.array_equal(g["logits"][:24], outs[0]["logits"])
+        assert np.array_equal(g["argmax_ids"][:24], outs[0]["argmax_ids"])
+        assert np.array_equal(g["logits_max"][:24], outs[0]["logits_max"])
+    o = orc.verify(np.ascontiguousarray(x[:48]), d["packed"], d["scales"], None, 48, 1, V, H, want_logits=True,
+                   n_threads=NTHREADS)
+    parity.check(outs[1], o, 48, 1, None)
+
+
 def test_batch_ties_across_tiles(vh, orc):
     """Copies of the winning row at indices in one vocabulary tile, in other
     tiles and in the last tile: every row's lowest copy must win."""
