@@ -71,6 +71,10 @@ CONFIGS = {
                        "full-vocab wide verify V=151936 H=5120 T=16"),
     "batch": Config("batch", 64, 4, 151936, 5120, 0.0, "geometric", 0.4, 5,
                     "batch verify 64 requests x T=4 V=151936 H=5120"),
+    # two requests verified at once, each a wide verify block: 32 rows, the
+    # smallest block past what one workgroup's registers hold
+    "two_blocks_t16": Config("two_blocks_t16", 2, 16, 151936, 5120, 0.05, "bernoulli_all", 0.9, 10,
+                             "two wide verify blocks (2 requests x T=16) V=151936 H=5120"),
     # one GPU's share of the full-vocabulary head split by vocabulary rows
     # over 8 GPUs (151936 / 8 = 18992 rows), at the wide verify block
     "shard_t16": Config("shard_t16", 1, 16, 18992, 5120, 0.05, "bernoulli_all", 0.9, 20,

@@ -4,7 +4,7 @@ the seeded input generator; the benchmark reads these files to build draft
 ids that agree with the target's argmax, and the tests check the files
 against fresh oracle runs.
 
-    python tests/golden/make_argmax.py full_t16 full_t8 tiny draft_vocab batch shard_t16
+    python tests/golden/make_argmax.py full_t16 full_t8 tiny draft_vocab batch shard_t16 two_blocks_t16
 """
 import json
 import os
@@ -37,4 +37,4 @@ def main(names):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or ["tiny", "draft_vocab", "full_t8", "full_t16", "batch", "shard_t16"])
+    main(sys.argv[1:] or ["tiny", "draft_vocab", "full_t8", "full_t16", "batch", "shard_t16", "two_blocks_t16"])

@@ -17,7 +17,8 @@ def _load(name):
 
 
 @pytest.mark.parametrize("name,trials", [("tiny", [0]), ("draft_vocab", [0, 1, 999]),
-                                         ("full_t16", [0]), ("shard_t16", [0, 19])])
+                                         ("full_t16", [0]), ("shard_t16", [0, 19]),
+                                         ("two_blocks_t16", [9])])
 def test_stored_argmax_matches_oracle(oracle_mod, name, trials):
     cfg = synth.CONFIGS[name]
     data = _load(name)

@@ -1,7 +1,8 @@
 """GPU parity on every seeded trial of the multi-trial workloads: the 1000
 repeats of the draft-vocabulary decode (V=8192, H=5120, T=1), the 20 trials
 of the full-vocabulary T=8 and T=16 verify blocks, the 5 trials of the
-64 x 4 batch, and the 20 trials of one GPU's vocabulary shard (V=18992, T=16).  Each GPU argmax is compared with the oracle's stored argmax
+64 x 4 batch, the 20 trials of one GPU's vocabulary shard (V=18992, T=16),
+and the 10 trials of two wide verify blocks at once (2 x T=16 = 32 rows).  Each GPU argmax is compared with the oracle's stored argmax
 (tests/golden/argmax_*.json, written by a script that calls only the
 oracle) under the near-tie rule: where the ids differ, the oracle logit at
 the GPU's id, recomputed for that one entry, must lie within
@@ -40,7 +41,7 @@ def vh():
     return binding
 
 
-@pytest.mark.parametrize("name", ["draft_vocab", "full_t8", "full_t16", "batch", "shard_t16"])
+@pytest.mark.parametrize("name", ["draft_vocab", "full_t8", "full_t16", "batch", "shard_t16", "two_blocks_t16"])
 def test_every_stored_trial(vh, oracle_mod, name):
     cfg = synth.CONFIGS[name]
     with open(os.path.join(GOLDEN, f"argmax_{name}.json")) as f:
