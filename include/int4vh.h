@@ -195,8 +195,9 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
                                size_t workspace_bytes, void *stream);
 
 /* Sampled (non-greedy) verification: the verify call with a sampling
- * epilogue fused into the same weight stream, for one block of R*T <= 16
- * rows (R requests of T positions).  The int4 head suffices because top-k
+ * epilogue fused into the same weight stream, for R*T <= 64 rows (R
+ * requests of T positions; beyond 16 rows in token groups of 16 sharing the
+ * tile stream, like the greedy call).  The int4 head suffices because top-k
  * sampling needs only the ordering of the logits ("HyperQwen: 1,000 tok/s on
  * a Single RTX 3090 Through Aggressive Recurrent-State Speculation",
  * Technical Insight, lm_head paragraph).  Per row r:
@@ -223,7 +224,7 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
  * NULL when top_k == 0); lse float32 [R*T] or NULL.
  * Errors as verify_lm_head_int4_batch, plus INT4VH_EINVAL for top_k outside
  * [0, min(16, V)], a temperature that is not finite and > 0, or a missing
- * sampled buffer, and INT4VH_EUNSUPPORTED for R*T > 16. */
+ * sampled buffer, and INT4VH_EUNSUPPORTED for R*T > 64. */
 int verify_lm_head_int4_sampled(const void *hidden, const uint8_t *packed_w, const void *scales,
                                 const int32_t *draft_ids, const float *draft_probs,
                                 const float *uniforms, int R, int T, int V, int H, int top_k,

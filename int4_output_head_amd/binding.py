@@ -318,7 +318,7 @@ def verify_mapped(hidden, packed_w, scales, vocab_ids, draft_ids=None, *, R: int
 def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, uniforms=None, *,
                    top_k: int, temperature: float = 1.0, R: int | None = None,
                    workspace: Workspace | None = None, events=None, want_lse: bool = False):
-    """Sampled verification for R*T <= 16 rows: top-k sampling at a
+    """Sampled verification for R*T <= 64 rows: top-k sampling at a
     temperature (top_k >= 1) or sampling over the whole vocabulary
     (top_k == 0).  hidden: float16 [R, T, H] (or [R*T, H] with R); draft_ids
     int32, draft_probs and uniforms float32, each [R, T-1] (None when T == 1).

@@ -127,9 +127,9 @@ constexpr int kGroupWgs = 16;                                     // workgroups 
 constexpr int kTicketStride = 32;                                 // uint32 per group ticket (128 B)
 constexpr size_t kWsGroupTk = kWsKeys + (size_t)kBatchMaxRows * 8;   // uint32 [64][32] group tickets
 constexpr size_t kWsDraftSeen = kWsGroupTk + (size_t)(kMaxGrid / kGroupWgs) * kTicketStride * 4;
-                                                                  // int32 [16] draft logit written
-constexpr size_t kWsDraftLogit = kWsDraftSeen + 64;                   // float [16] the draft's logit
-constexpr size_t kWsCtlBytes = kWsDraftSeen + 256;
+                                                                  // int32 [64] draft logit written
+constexpr size_t kWsDraftLogit = kWsDraftSeen + 256;                  // float [64] the draft's logit
+constexpr size_t kWsCtlBytes = kWsDraftSeen + 512;
 constexpr size_t kWsExp = kWsCtlBytes;                            // int32 [4096] step exponents
 constexpr size_t kWsPart = kWsExp + (size_t)kBatchMaxRows * 4;    // uint64 [kMaxGrid][16]
 constexpr size_t kWsFrag = kWsPart + (size_t)kMaxGrid * kMaxRows * 8;   // activation fragments
@@ -279,8 +279,8 @@ struct Args {
     const int32_t *vmap;      // [V] token id of each head row, or null (identity)
     uint64_t *part;           // [grid, M] packed (index << 32 | value bits)
     // sampled epilogue (top-k sampling at a temperature; unused when off)
-    unsigned long long *part_topk;   // [grid, M, kTopK] per-workgroup top-k keys
-    unsigned long long *group_topk;  // [grid / 16, M, kTopK] per-group top-k keys
+    unsigned long long *part_topk;   // [groups * sets, rows per workgroup, kTopK] per-workgroup top-k keys
+    unsigned long long *group_topk;  // [merge groups, rows per workgroup, kTopK] per-merge-group keys
     uint32_t *group_ticket;          // [64][kTicketStride] per-group tickets (word 0), zero between calls
     int top_k;                // k <= kTopK
     float tau;                // temperature > 0
@@ -290,10 +290,10 @@ struct Args {
     float *topk_logits;       // [M, k]
     float *p_draft;           // [R, T-1]
     float *lse_out;           // [M] log sum exp(logit / tau), or null
-    uint64_t *part_lse;       // [grid, M] per-workgroup (max, sum) of exp2 terms
-    uint64_t *group_lse;      // [grid / 16, M]
-    int32_t *draft_seen;      // [16] set when the draft's logit was written; zero between calls
-    float *draft_logit;       // [16]
+    uint64_t *part_lse;       // [groups * sets, rows per workgroup] per-workgroup (max, sum) of exp2 terms
+    uint64_t *group_lse;      // [merge groups, rows per workgroup]
+    int32_t *draft_seen;      // [M <= 64] set when the draft's logit was written; zero between calls
+    float *draft_logit;       // [M]
     uint32_t *ticket;
     int32_t *exps;            // [16]
     const u32x4 *frag;        // activation fragments
@@ -508,14 +508,15 @@ __device__ __forceinline__ uint64_t lse_pack(float m, float s)
     return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)__float_as_uint(m);
 }
 
-// (m, s) pairs [n <= 16] of one row, stored [n][M] from `pairs`: lane j of
-// each 16-lane group loads pair j of row `row` (all loads in flight at once)
-// and a fixed sequence of row rotations combines them; every lane of the
-// group ends with the same pair.  Called by all lanes of the wave.
-__device__ __forceinline__ uint64_t lse_load16(const uint64_t *pairs, int n, int M, int row)
+// (m, s) pairs [n <= 16] of one row, stored [n][stride] from `pairs`: lane
+// j of each 16-lane group loads pair j of row `row` (all loads in flight at
+// once) and a fixed sequence of row rotations combines them; every lane of
+// the group ends with the same pair.  Called by all lanes of the wave.
+__device__ __forceinline__ uint64_t lse_load16(const uint64_t *pairs, int n, int stride, int row)
 {
     const int j = threadIdx.x & 15;
-    return __hip_atomic_load(&pairs[(size_t)(j < n ? j : 0) * M + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_load(&pairs[(size_t)(j < n ? j : 0) * stride + row], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void lse_combine16(uint64_t pr, int n, float &m, float &s)
 {
@@ -525,14 +526,15 @@ __device__ __forceinline__ void lse_combine16(uint64_t pr, int n, float &m, floa
     row_lse16(m, s);
 }
 
-// Merge up to 16 published top-k lists ([n_lists][M][kTopK] keys, rank
-// order) per token; a workgroup of 512 threads, wave w handling tokens 2w
-// and 2w+1 with 32 lanes each.  Each half of the 32 lanes folds the lists of
-// its parity (all loads issued first), then the halves merge; every lane
-// returns the rank-(lane & 15) key of its token's merged list.
+// Merge up to 16 published top-k lists ([n_lists][stride][kTopK] keys, rank
+// order) per token of the first M <= 16; a workgroup of 512 threads, wave w
+// handling tokens 2w and 2w+1 with 32 lanes each.  Each half of the 32 lanes
+// folds the lists of its parity (all loads issued first), then the halves
+// merge; every lane returns the rank-(lane & 15) key of its token's merged
+// list.
 template <int kTopK>
 __device__ __forceinline__ unsigned long long merge_topk_lists(const unsigned long long *lists, int n_lists,
-                                                               int M, int lane)
+                                                               int stride, int M, int lane)
 {
     const int wave = threadIdx.x >> 6;
     const int m = 2 * wave + (lane >> 5);
@@ -547,7 +549,7 @@ __device__ __forceinline__ unsigned long long merge_topk_lists(const unsigned lo
         const int w = 2 * i + h;
         const int r = (i & 1) == 0 ? j : 15 - j;
         const bool live = w < n_lists && r < kTopK;
-        const unsigned long long v = __hip_atomic_load(&lists[((size_t)(live ? w : 0) * M + mm) * kTopK + (live ? r : 0)],
+        const unsigned long long v = __hip_atomic_load(&lists[((size_t)(live ? w : 0) * stride + mm) * kTopK + (live ? r : 0)],
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         e[i] = live ? v : 0ull;
     }
@@ -750,8 +752,8 @@ verify_kernel(Args a)
     struct Merge {
         float fv[kWaves][kMaxRows];
         int fi[kWaves][kMaxRows];
-        int draft[kMaxRows];
-        int accept[kMaxRows];
+        int draft[kMaxGroups * kMaxRows];
+        int accept[kMaxGroups * kMaxRows];
         int last;
         int arg_g[kMaxGroups * kMaxRows];     // several token groups: ids of every row
         int draft_g[kMaxGroups * kMaxRows];   // and the drafts of every request
@@ -845,8 +847,9 @@ verify_kernel(Args a)
     // sampled epilogue: the draft id of the lane's token (loaded ahead of the
     // weight copies, like every other register the main loop reads)
     int my_draft = -1;
-    if (kTopK > 0 && rlane && a.T > 1 && (rtok % a.T) < a.T - 1)
-        my_draft = a.draft[(rtok / a.T) * (a.T - 1) + rtok % a.T];
+    const int grow = kMaxRows * tgrp + rtok;                 // the lane's row of the call
+    if (kTopK > 0 && rlane && a.T > 1 && (grow % a.T) < a.T - 1)
+        my_draft = a.draft[(grow / a.T) * (a.T - 1) + grow % a.T];
     if constexpr (!kFused) {
         // from stage_kernel, in the workspace
 #pragma unroll
@@ -1071,8 +1074,8 @@ verify_kernel(Args a)
                     if constexpr (kLse)
                         lse_combine(lm, ls, val * zscale, 1.0f);
                     if (kLse && v == my_draft) {      // one lane of one workgroup per token
-                        __hip_atomic_store(&a.draft_logit[rtok], val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        __hip_atomic_store(&a.draft_seen[rtok], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&a.draft_logit[grow], val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_store(&a.draft_seen[grow], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
                 if (kLogits)
@@ -1213,14 +1216,16 @@ verify_kernel(Args a)
     if constexpr (kTopK > 0) {
         // lane n16 = j publishes the rank-j key of the workgroup's list;
         // the 16 lanes' (max, sum) pairs combine (fixed rotations) and lane
-        // 0 of the token publishes them
+        // 0 of the token publishes them.  Slots are ordered by (token group,
+        // tile set), so each merge group's lists are contiguous.
+        const size_t pslot = (size_t)tgrp * n_sets + tset;
         if (rlane && n16 < kTopK)
-            __hip_atomic_store(&a.part_topk[((size_t)b * M + rtok) * kTopK + n16], dl,
+            __hip_atomic_store(&a.part_topk[(pslot * pstride + rtok) * kTopK + n16], dl,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if constexpr (kLse) {
             row_lse16(lm, ls);
             if (rlane && n16 == 0)
-                __hip_atomic_store(&a.part_lse[(size_t)b * M + rtok], lse_pack(lm, ls), __ATOMIC_RELAXED,
+                __hip_atomic_store(&a.part_lse[pslot * pstride + rtok], lse_pack(lm, ls), __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -1265,12 +1270,14 @@ verify_kernel(Args a)
             return;
     } else {
         // Two levels, so that most of the merging overlaps the weight stream
-        // of the workgroups still running: the last workgroup of each group
-        // of 16 merges the group's lists into one, and the last group to
-        // finish runs the final merge.
-        const int grp = b / 16;
-        const int gsz = min(16, G - 16 * grp);
-        const int n_grp = (G + 15) / 16;
+        // of the workgroups still running: the last workgroup of each merge
+        // group (up to 16 tile sets of one token group) merges the group's
+        // lists into one, and the last merge group to finish runs the final
+        // merge.
+        const int n_mg = (n_sets + 15) / 16;          // merge groups per token group
+        const int grp = tgrp * n_mg + tset / 16;
+        const int gsz = min(16, n_sets - 16 * (tset / 16));
+        const int n_grp = n_g * n_mg;
         if (threadIdx.x == 0) {
             const uint32_t prev = __hip_atomic_fetch_add(&a.group_ticket[(size_t)grp * kTicketStride], 1u,
                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1281,20 +1288,22 @@ verify_kernel(Args a)
             return;
         {
             const int m = 2 * wave + (lane >> 5);
+            const size_t first = (size_t)tgrp * n_sets + 16 * (tset / 16);   // the group's first slot
             // the pairs' loads go out with the lists' (one round trip)
-            const uint64_t lse_pr = kLse ? lse_load16(a.part_lse + (size_t)16 * grp * M, gsz, M, m < M ? m : 0) : 0;
-            const unsigned long long mine = merge_topk_lists<kTopK>(a.part_topk + (size_t)16 * grp * M * kTopK,
-                                                                    gsz, M, lane);
-            if (m < M && ((lane >> 4) & 1) == 0 && n16 < kTopK)
-                __hip_atomic_store(&a.group_topk[((size_t)grp * M + m) * kTopK + n16], mine,
+            const uint64_t lse_pr =
+                kLse ? lse_load16(a.part_lse + first * pstride, gsz, pstride, m < Mg ? m : 0) : 0;
+            const unsigned long long mine =
+                merge_topk_lists<kTopK>(a.part_topk + first * pstride * kTopK, gsz, pstride, Mg, lane);
+            if (m < Mg && ((lane >> 4) & 1) == 0 && n16 < kTopK)
+                __hip_atomic_store(&a.group_topk[((size_t)grp * pstride + m) * kTopK + n16], mine,
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if constexpr (kLse) {
                 // lane n16 of the token's 16-lane group loads workgroup n16's
                 // pair; fixed row rotations combine the 16
                 float gm, gs;
                 lse_combine16(lse_pr, gsz, gm, gs);
-                if (m < M && (lane & 31) == 0)
-                    __hip_atomic_store(&a.group_lse[(size_t)grp * M + m], lse_pack(gm, gs), __ATOMIC_RELAXED,
+                if (m < Mg && (lane & 31) == 0)
+                    __hip_atomic_store(&a.group_lse[(size_t)grp * pstride + m], lse_pack(gm, gs), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -1463,69 +1472,76 @@ verify_kernel(Args a)
             accept_from_ballot(__ballot(match), T, a.R, m, a.n_acc);
         }
     } else {
-        // Sampled epilogue, final merge over the group lists, then the
-        // token's target probability of its draft from the k logits (top-k
-        // sampling at temperature tau): lane j of the token's first 16-lane
-        // group holds rank j; sums are fixed rotations over the 16 lanes.
-        const int n_grp = (G + 15) / 16;
-        const int m = 2 * wave + (lane >> 5);
-        const int slot = lane & 31;                   // 0..15: first group of the token
-        const int mm = m < M ? m : M - 1;
+        // Sampled epilogue, final merge over the merge groups' lists, then
+        // the token's target probability of its draft from the k logits
+        // (top-k sampling at temperature tau): lane j of the token's first
+        // 16-lane group holds rank j; sums are fixed rotations over the 16
+        // lanes.  One pass per token group of 16 rows.
+        const int n_mg = (n_sets + 15) / 16;          // merge groups per token group
         const int T = a.T;
-        const int req = mm / T, t = mm % T;
-        const bool drafted = t < T - 1;
-        const int di = drafted ? req * (T - 1) + t : 0;
-        // every load of this stage is issued before the lists' (one round trip)
-        const float u_d = drafted ? a.unif[di] : 1.0f, q_d = drafted ? a.dprob[di] : 1.0f;
-        uint64_t lse_pr = 0;
-        int seen_d = 0;
-        float logit_d = 0.0f;
-        if constexpr (kLse) {
-            lse_pr = lse_load16(a.group_lse, n_grp, M, mm);
-            seen_d = __hip_atomic_load(&a.draft_seen[mm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            logit_d = __hip_atomic_load(&a.draft_logit[mm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        const unsigned long long mine = merge_topk_lists<kTopK>(a.group_topk, n_grp, M, lane);
-        const int d = drafted ? s_draft[di] : -1;
-        const float hv = key_value(mine);
-        const int hi = key_index(mine);
-        if (slot == 0 && m < M) {                     // rank 0: the greedy winner
-            a.logits_max[m] = hv;
-            a.argmax[m] = a.vmap ? a.vmap[hi] : hi;
-        }
-        const float lmax = key_value(key_shfl(mine, lane & ~15));
-        const float e = n16 < a.top_k ? expf((hv - lmax) / a.tau) : 0.0f;
-        float sum = e, e_d = (n16 < a.top_k && hi == d) ? e : 0.0f;
-        sum = row_sum16(sum);
-        e_d = row_sum16(e_d);
-        if (slot < a.top_k && m < M) {
-            a.topk_ids[m * a.top_k + slot] = hi;
-            a.topk_logits[m * a.top_k + slot] = hv;
-        }
-        // log sum exp(logit / tau) over the whole vocabulary, from the
-        // group pairs (lane-parallel loads, fixed row rotations)
-        float lse = 0.0f;
-        if constexpr (kLse) {
-            float gm, gs;
-            lse_combine16(lse_pr, n_grp, gm, gs);
-            lse = (gm + __log2f(gs)) * 0.6931471805599453f;
-        }
-        if (slot == 0 && m < M) {
-            if (kLse && a.lse_out)
-                a.lse_out[m] = lse;
-            int ok = 0;
-            if (drafted) {
-                float p;
-                if (!kLse || a.top_k > 0)
-                    p = e_d / sum;
-                else
-                    p = seen_d != 0 ? expf(logit_d / a.tau - lse) : 0.0f;
-                a.p_draft[di] = p;
-                ok = u_d * q_d < p;
+        for (int tg = 0; tg < n_g; ++tg) {
+            const int Mt = min(kMaxRows, M - kMaxRows * tg);           // rows of token group tg
+            const int ml = 2 * wave + (lane >> 5);                     // row within the group
+            const int slot = lane & 31;                                // 0..15: first 16 lanes of the row
+            const int mml = ml < Mt ? ml : Mt - 1;
+            const int m = kMaxRows * tg + ml, mm = kMaxRows * tg + mml;  // rows of the call
+            const int req = mm / T, t = mm % T;
+            const bool drafted = t < T - 1;
+            const int di = drafted ? req * (T - 1) + t : 0;
+            // every load of this pass is issued before the lists' (one round trip)
+            const float u_d = drafted ? a.unif[di] : 1.0f, q_d = drafted ? a.dprob[di] : 1.0f;
+            uint64_t lse_pr = 0;
+            int seen_d = 0;
+            float logit_d = 0.0f;
+            if constexpr (kLse) {
+                lse_pr = lse_load16(a.group_lse + (size_t)tg * n_mg * pstride, n_mg, pstride, mml);
+                seen_d = __hip_atomic_load(&a.draft_seen[mm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                logit_d = __hip_atomic_load(&a.draft_logit[mm], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            s_accept[m] = ok;
-            if constexpr (kLse)
-                __hip_atomic_store(&a.draft_seen[m], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const unsigned long long mine = merge_topk_lists<kTopK>(
+                a.group_topk + (size_t)tg * n_mg * pstride * kTopK, n_mg, pstride, Mt, lane);
+            const int d = drafted ? s_draft[di] : -1;
+            const float hv = key_value(mine);
+            const int hi = key_index(mine);
+            const bool live = ml < Mt;
+            if (slot == 0 && live) {                      // rank 0: the greedy winner
+                a.logits_max[m] = hv;
+                a.argmax[m] = a.vmap ? a.vmap[hi] : hi;
+            }
+            const float lmax = key_value(key_shfl(mine, lane & ~15));
+            const float e = n16 < a.top_k ? expf((hv - lmax) / a.tau) : 0.0f;
+            float sum = e, e_d = (n16 < a.top_k && hi == d) ? e : 0.0f;
+            sum = row_sum16(sum);
+            e_d = row_sum16(e_d);
+            if (slot < a.top_k && live) {
+                a.topk_ids[m * a.top_k + slot] = hi;
+                a.topk_logits[m * a.top_k + slot] = hv;
+            }
+            // log sum exp(logit / tau) over the whole vocabulary, from the
+            // merge groups' pairs (lane-parallel loads, fixed row rotations)
+            float lse = 0.0f;
+            if constexpr (kLse) {
+                float gm, gs;
+                lse_combine16(lse_pr, n_mg, gm, gs);
+                lse = (gm + __log2f(gs)) * 0.6931471805599453f;
+            }
+            if (slot == 0 && live) {
+                if (kLse && a.lse_out)
+                    a.lse_out[m] = lse;
+                int ok = 0;
+                if (drafted) {
+                    float p;
+                    if (!kLse || a.top_k > 0)
+                        p = e_d / sum;
+                    else
+                        p = seen_d != 0 ? expf(logit_d / a.tau - lse) : 0.0f;
+                    a.p_draft[di] = p;
+                    ok = u_d * q_d < p;
+                }
+                s_accept[m] = ok;
+                if constexpr (kLse)
+                    __hip_atomic_store(&a.draft_seen[m], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
         __syncthreads();
         if (threadIdx.x < 64)
@@ -2068,6 +2084,30 @@ Pair make_grouped()
     return Pair{stage_kernel<16, kUnits>, verify_kernel<16, kUnits, kRing, kLogits, 0, false, false, 0>};
 }
 
+// Token groups with the sampled epilogue (8- or 16-entry lists, with or
+// without the whole-vocabulary log-sum-exp).
+template <int kUnits, int kTopK, bool kLse>
+Pair make_grouped_sampled()
+{
+    constexpr int kRing = kUnits <= 5 ? 3 : 2;
+    return Pair{stage_kernel<16, kUnits>, verify_kernel<16, kUnits, kRing, false, kTopK, kLse, false, 0>};
+}
+
+template <int kTopK, bool kLse>
+Pair pick_grouped_sampled(int units)
+{
+    switch (units) {
+    case 1: return make_grouped_sampled<1, kTopK, kLse>();
+    case 2: return make_grouped_sampled<2, kTopK, kLse>();
+    case 3: return make_grouped_sampled<3, kTopK, kLse>();
+    case 4: return make_grouped_sampled<4, kTopK, kLse>();
+    case 5: return make_grouped_sampled<5, kTopK, kLse>();
+    case 6: return make_grouped_sampled<6, kTopK, kLse>();
+    case 7: return make_grouped_sampled<7, kTopK, kLse>();
+    default: return make_grouped_sampled<8, kTopK, kLse>();
+    }
+}
+
 template <bool kLogits>
 Pair pick_grouped(int units)
 {
@@ -2167,6 +2207,14 @@ int rows_steps(int H)
 // 16 sharing the tile stream); larger calls run the matrix-core batch path.
 constexpr int kStreamMaxRows = kMaxRows * kMaxGroups;
 
+// The sampled epilogue's area (per-workgroup and per-merge-group lists and
+// pairs) follows the activation fragments of the call's token groups.
+constexpr size_t kSampledArea = kWsBytes - kWsTopK;
+size_t sampled_base(int n_groups)
+{
+    return kWsFrag + (size_t)n_groups * kFragBytes;
+}
+
 size_t workspace_need(int R, int T, int V, int H)
 {
     if (R < 1 || T < 1 || T > INT4VH_MAX_T || V < 1 || H < 32 || (H % 32) != 0)
@@ -2176,8 +2224,8 @@ size_t workspace_need(int R, int T, int V, int H)
         return 0;
     if (M <= kMaxRows)
         return kWsBytes;
-    if (M <= kStreamMaxRows)   // one fragment area per token group
-        return kWsFrag + (size_t)((M + kMaxRows - 1) / kMaxRows) * kFragBytes;
+    if (M <= kStreamMaxRows)   // one fragment area per token group, then the sampled epilogue's area
+        return sampled_base((int)((M + kMaxRows - 1) / kMaxRows)) + kSampledArea;
     const size_t n_mt = (size_t)((M + kRTokTile - 1) / kRTokTile);
     return kWsFrag + n_mt * (size_t)kRTbPerTile * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
 }
@@ -2309,7 +2357,7 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
         return st;
     if (vmap && !aligned(vmap, 4))
         return INT4VH_EALIGN;
-    if (smp && R * T > kMaxRows)
+    if (smp && R * T > kStreamMaxRows)
         return INT4VH_EUNSUPPORTED;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -2323,8 +2371,6 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
                            wsb, dev, s, ev0, ev1);
     Args a;
     a.vmap = vmap;
-    a.part_topk = reinterpret_cast<unsigned long long *>(wsb + kWsTopK);
-    a.group_topk = reinterpret_cast<unsigned long long *>(wsb + kWsGroupTopK);
     a.group_ticket = reinterpret_cast<uint32_t *>(wsb + kWsGroupTk);
     a.top_k = smp ? smp->top_k : 0;
     a.tau = smp ? smp->tau : 1.0f;
@@ -2334,8 +2380,6 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     a.topk_logits = smp ? smp->topk_logits : nullptr;
     a.p_draft = smp ? smp->p_draft : nullptr;
     a.lse_out = smp ? smp->lse : nullptr;
-    a.part_lse = reinterpret_cast<uint64_t *>(wsb + kWsLse);
-    a.group_lse = reinterpret_cast<uint64_t *>(wsb + kWsGroupLse);
     a.draft_seen = reinterpret_cast<int32_t *>(wsb + kWsDraftSeen);
     a.draft_logit = reinterpret_cast<float *>(wsb + kWsDraftLogit);
     a.hidden = static_cast<const uint16_t *>(hidden);
@@ -2368,10 +2412,20 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     // XCD; at most 128 sets, the final merge's capacity)
     a.n_groups = (a.M + kMaxRows - 1) / kMaxRows;
     a.group_words = kFragBytes / sizeof(u32x4);
+    {
+        // the sampled epilogue's area follows the groups' fragments
+        char *sb = wsb + sampled_base(a.n_groups);
+        a.part_topk = reinterpret_cast<unsigned long long *>(sb);
+        a.group_topk = reinterpret_cast<unsigned long long *>(sb + (kWsGroupTopK - kWsTopK));
+        a.part_lse = reinterpret_cast<uint64_t *>(sb + (kWsLse - kWsTopK));
+        a.group_lse = reinterpret_cast<uint64_t *>(sb + (kWsGroupLse - kWsTopK));
+    }
     if (a.n_groups > 1) {
         int sets = grid / a.n_groups;
         if (sets > kMaxGrid / kMaxGroups)
             sets = kMaxGrid / kMaxGroups;
+        if (smp && sets > kSampledMaxGrid / a.n_groups)   // the sampled area's capacity
+            sets = kSampledMaxGrid / a.n_groups;
         if (sets > a.n_tiles)
             sets = a.n_tiles;
         if (sets >= 8)
@@ -2387,7 +2441,13 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     }
     int kp = 16;
     const bool fused = !smp && a.n_groups == 1 && fused_staging(a.M, units);
-    const Pair fn = fused            ? (lout ? pick_fused<true>(units) : pick_fused<false>(units))
+    const bool smp_lse = smp && (smp->top_k == 0 || smp->lse != nullptr);
+    const Pair fn = fused ? (lout ? pick_fused<true>(units) : pick_fused<false>(units))
+                    : (a.n_groups > 1 && smp)
+                        ? (smp->top_k > 8 ? (smp_lse ? pick_grouped_sampled<16, true>(units)
+                                                     : pick_grouped_sampled<16, false>(units))
+                                          : (smp_lse ? pick_grouped_sampled<8, true>(units)
+                                                     : pick_grouped_sampled<8, false>(units)))
                     : a.n_groups > 1 ? (lout ? pick_grouped<true>(units) : pick_grouped<false>(units))
                                      : pick_kernels(a.M, units, lout != nullptr, smp != nullptr, smp ? smp->top_k : 0,
                                                     smp && (smp->top_k == 0 || smp->lse != nullptr), &kp);

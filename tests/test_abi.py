@@ -227,7 +227,7 @@ def test_sampled_rejects_invalid_arguments(lib):
     assert scall(pdr=0) == EINVAL
     assert scall(tids=0) == EINVAL
     assert scall(tlog=A + 2) == EALIGN
-    assert scall(R=2, T=9) == EUNSUPPORTED            # more than 16 rows
+    assert scall(R=5, T=13) == EUNSUPPORTED           # more than 64 rows
     assert scall(R=1, T=17) == EINVAL
     assert scall(ws_bytes=100) == EWORKSPACE
 

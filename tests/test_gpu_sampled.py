@@ -212,7 +212,11 @@ def check(g, o, lg, d, q, u, R, T, k, tau):
                                            (2, 8, 4097, 256, 5, 1.3), (4, 4, 999, 96, 16, 1.0),
                                            (1, 1, 8192, 5120, 8, 1.0), (3, 5, 2000, 160, 1, 1.0),
                                            (16, 1, 700, 128, 12, 2.0), (1, 16, 5000, 512, 16, 0.3),
-                                           (2, 8, 4097, 256, 8, 2.0), (1, 16, 20000, 1024, 16, 1.3)])
+                                           (2, 8, 4097, 256, 8, 2.0), (1, 16, 20000, 1024, 16, 1.3),
+                                           # more than 16 rows: token groups of 16
+                                           (2, 16, 5000, 512, 16, 1.0), (3, 11, 4097, 256, 8, 0.7),
+                                           (4, 16, 3000, 128, 16, 1.3), (17, 1, 2000, 96, 5, 2.0),
+                                           (5, 12, 20000, 1024, 16, 0.3)])
 def test_sampled_parity(vh, oracle_mod, R, T, V, H, k, tau):
     say(f"sampled R={R} T={T} V={V} H={H} k={k} tau={tau}")
     inp = synth.uniform_inputs(R * T, V, H, seed=R * 31 + T + V + H + k)
@@ -260,7 +264,9 @@ def check_full_softmax(g, o, lg, d, q, u, R, T, tau):
 
 @pytest.mark.parametrize("R,T,V,H,tau", [(1, 16, 5000, 512, 1.0), (2, 8, 4097, 256, 0.3),
                                          (4, 4, 999, 96, 2.0), (1, 8, 151936, 5120, 1.0),
-                                         (1, 16, 20000, 1024, 0.7), (2, 4, 3000, 256, 1.3)])
+                                         (1, 16, 20000, 1024, 0.7), (2, 4, 3000, 256, 1.3),
+                                         (2, 16, 5000, 512, 1.0), (4, 16, 3000, 256, 0.7),
+                                         (3, 7, 4097, 96, 2.0)])
 def test_full_softmax_parity(vh, oracle_mod, R, T, V, H, tau):
     """Sampling over the whole vocabulary (top_k = 0): the fused online
     log-sum-exp and the draft's probability against the oracle."""
@@ -284,6 +290,27 @@ def test_full_softmax_parity(vh, oracle_mod, R, T, V, H, tau):
     say(f"full softmax max relative error of p: {rel:.2e}; on the GPU's own logits {own}")
 
 
+def test_sampled_full_vocab_two_blocks(vh, oracle_mod):
+    """Two T=16 blocks at the full vocabulary (two token groups sharing the
+    tile stream), top-16 at tau = 1 and the whole-vocabulary log-sum-exp."""
+    cfg = synth.CONFIGS["two_blocks_t16"]
+    head = synth.make_head(cfg)
+    x = synth.make_hidden(cfg, 0)
+    lg = oracle_mod.logits(x, head["packed"], head["scales"], cfg.M, cfg.V, cfg.H, n_threads=16)
+    inp = dict(hidden=x, packed=head["packed"], scales=head["scales"])
+    d, q, u = make_drafts(lg, cfg.R, cfg.T, 16, seed=4)
+    ids, vals = sm.topk_rows(lg, 16)
+    idx, mx, gap, amax = oracle_mod.argmax_rows(lg)
+    p, n = sm.sampled_accept(ids, vals, d, q, u, cfg.R, cfg.T, 1.0)
+    o = dict(logits=lg, logits_max=mx, argmax_ids=idx, gap=gap, amax=amax, topk_ids=ids,
+             topk_logits=vals, p_draft=p, n_accepted=n, lse=sm.lse_rows(lg, 1.0))
+    g = run(vh, inp, d, q, u, cfg.R, cfg.T, cfg.V, cfg.H, 16, 1.0)
+    st = check(g, o, lg, d, q, u, cfg.R, cfg.T, 16, 1.0)
+    st["lse_max_err"] = check_lse(g, o, lg, 1.0)
+    st.update(check_own_logits(g, d, cfg.R, cfg.T, 16, 1.0))
+    say(f"full-vocab 2 x T=16 stats {st}")
+
+
 def test_sampled_full_vocab_t16(vh, oracle_mod):
     """The headline shape: V=151936, H=5120, T=16, top-16 at tau = 1."""
     cfg = synth.CONFIGS["full_t16"]
@@ -303,10 +330,12 @@ def test_sampled_full_vocab_t16(vh, oracle_mod):
     say(f"full-vocab T=16 stats {st}")
 
 
-def test_sampled_int_exact_bitexact(vh, oracle_mod):
+@pytest.mark.parametrize("R,T", [(2, 8), (3, 16)])
+def test_sampled_int_exact_bitexact(vh, oracle_mod, R, T):
     """Integer-exact inputs: the top-k ids (ties broken by the lowest row
-    across tiles and workgroups) and logits equal the oracle's bit for bit."""
-    R, T, V, H, k = 2, 8, 3000, 512, 16
+    across tiles and workgroups) and logits equal the oracle's bit for bit
+    (one block of 16 rows, and three token groups)."""
+    V, H, k = 3000, 512, 16
     inp = synth.int_exact_inputs(R * T, V, H, seed=12)
     lg = oracle_mod.logits(inp["hidden"], inp["packed"], inp["scales"], R * T, V, H)
     d, q, u = make_drafts(lg, R, T, k, seed=2)
@@ -366,22 +395,24 @@ def test_k1_is_greedy_acceptance(vh):
     assert torch.all(out[4][0, :9] == 1.0) and float(out[4][0, 9]) == 0.0
 
 
-def test_sampled_then_greedy_workspace_reuse(vh):
+@pytest.mark.parametrize("R,T", [(1, 8), (3, 12)])
+def test_sampled_then_greedy_workspace_reuse(vh, R, T):
     """Sampled and greedy calls alternate on one workspace; each call leaves
-    it ready for the next (results equal fresh calls)."""
-    R, T, V, H = 1, 8, 6000, 256
-    inp = synth.uniform_inputs(T, V, H, seed=5)
-    x = dev(inp["hidden"], torch.float16)
+    it ready for the next (results equal fresh calls), with one block and
+    with token groups."""
+    V, H = 6000, 256
+    inp = synth.uniform_inputs(R * T, V, H, seed=5 + R)
+    x = dev(inp["hidden"], torch.float16).reshape(R, T, H)
     w = dev(inp["packed"])
     s = dev(inp["scales"], torch.float16)
-    d = dev(np.arange(T - 1, dtype=np.int32))
-    q = torch.ones(T - 1, dtype=torch.float32, device="cuda")
-    u = torch.rand(T - 1, dtype=torch.float32, device="cuda")
-    ws = vh.Workspace(vh.workspace_bytes(1, T, V, H), x.device)
-    a1 = vh.verify_sampled(x.reshape(1, T, H), w, s, d, q, u, top_k=16, workspace=ws)
-    b1 = vh.verify(x, w, s, d, workspace=ws)
-    a2 = vh.verify_sampled(x.reshape(1, T, H), w, s, d, q, u, top_k=16, workspace=ws)
-    b2 = vh.verify(x, w, s, d, workspace=ws)
+    d = dev((np.arange(R * (T - 1), dtype=np.int32) % V).reshape(R, T - 1))
+    q = torch.ones((R, T - 1), dtype=torch.float32, device="cuda")
+    u = torch.rand((R, T - 1), dtype=torch.float32, device="cuda")
+    ws = vh.Workspace(vh.workspace_bytes(R, T, V, H), x.device)
+    a1 = vh.verify_sampled(x, w, s, d, q, u, top_k=16, workspace=ws)
+    b1 = vh.verify_batch(x, w, s, d, workspace=ws)
+    a2 = vh.verify_sampled(x, w, s, d, q, u, top_k=16, workspace=ws)
+    b2 = vh.verify_batch(x, w, s, d, workspace=ws)
     torch.cuda.synchronize()
     for p1, p2 in zip(a1, a2):
         assert (p1 is None and p2 is None) or torch.equal(p1, p2)
