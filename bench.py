@@ -96,22 +96,24 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_096_226, write=73_920, source="int4vh.hip",
-                      source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
-    "full_t8": dict(read=390_422_958, write=41_088, source="int4vh.hip",
-                     source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
-    "two_blocks_t16": dict(read=393_093_819, write=74_048, source="int4vh.hip",
-                            source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
-    "batch": dict(read=684_020_959, write=1_062_176, source="int4vh.hip",
-                   source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
-    "draft_vocab": dict(read=21_334_418, write=17_536, source="int4vh.hip",
-                         source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
-    "shard_t16": dict(read=50_759_602, write=74_944, source="int4vh.hip",
-                       source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
-    "full_t16_top16": dict(read=391_741_313, write=568_576, source="int4vh.hip",
-                            source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
-    "full_t16_top0": dict(read=391_545_485, write=358_912, source="int4vh.hip",
-                           source_sha256="98d47ace28884c0969c1c6d554a472855d5ca5527c64c6d6385ae03d6e3406a2"),
+    "full_t16": dict(read=391_092_634, write=73_933, source="int4vh.hip",
+                      source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "full_t8": dict(read=390_418_842, write=41_062, source="int4vh.hip",
+                     source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "two_blocks_t16": dict(read=393_102_541, write=74_035, source="int4vh.hip",
+                            source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "batch": dict(read=684_017_459, write=1_062_195, source="int4vh.hip",
+                   source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "draft_vocab": dict(read=21_349_786, write=17_510, source="int4vh.hip",
+                         source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "shard_t16": dict(read=50_755_994, write=74_957, source="int4vh.hip",
+                       source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "full_t16_top16": dict(read=391_748_403, write=568_525, source="int4vh.hip",
+                            source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "full_t16_top0": dict(read=391_521_280, write=358_912, source="int4vh.hip",
+                           source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "two_blocks_t16_top16": dict(read=393_702_605, write=570_778, source="int4vh.hip",
+                                  source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
