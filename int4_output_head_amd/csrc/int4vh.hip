@@ -851,7 +851,14 @@ verify_kernel(Args a)
     if (kTopK > 0 && rlane && a.T > 1 && (grow % a.T) < a.T - 1)
         my_draft = a.draft[(grow / a.T) * (a.T - 1) + grow % a.T];
     if constexpr (!kFused) {
-        // from stage_kernel, in the workspace
+        // Tile 0's copies go out first, so that HBM starts streaming while
+        // the fragments (245 KB per workgroup at 16 rows, from L2) pass the
+        // CU's in-order memory pipeline; the next prologue tiles follow them,
+        // so that waiting for tile 0 at the first step also covers the
+        // fragments.  (Issuing every prologue tile first delays the fragments
+        // by a second tile and measured slower.)
+        issue_tile(0, true);
+        // fragments from stage_kernel, in the workspace
 #pragma unroll
         for (int i = 0; i < kUnits; ++i)
 #pragma unroll
@@ -860,11 +867,11 @@ verify_kernel(Args a)
                 for (int g = 0; g < kGroups; ++g)
                     afr[i][t][g] = __builtin_bit_cast(
                         i32x4, a.frag[(size_t)tgrp * a.group_words + frag_index<kP, kUnits>(wave, i, t, g, lane)]);
-        // the prologue tiles, unconditional like the first step's (a tile
-        // past the head reads clamped bytes into a ring slot that is never
-        // used; every copy has landed before the workgroup publishes)
+        // the other prologue tiles, unconditional like the first step's (a
+        // tile past the head reads clamped bytes into a ring slot that is
+        // never used; every copy has landed before the workgroup publishes)
 #pragma unroll
-        for (int k = 0; k < kRing - 1; ++k)
+        for (int k = 1; k < kRing - 1; ++k)
             issue_tile(k, true);
         // the step exponents of the wave's two tokens, by a scalar load once
         // the copies are out (a vector load would make the compiler wait for
@@ -1145,7 +1152,9 @@ verify_kernel(Args a)
         // after the barrier every wave's copies are, and tile k-1's partial
         // sums are complete in s_part
         // copies issued after tile k's: min(kRing - 2, n_my - 1 - k) tiles,
-        // kRing - 2 at the first step (the prologue is unconditional)
+        // kRing - 2 at the first step (the prologue is unconditional; the
+        // fragment loads, issued between tile 0's copies and tile 1's, are
+        // done once tile 0's are)
         static_assert(kRing >= 2 && kRing <= 4, "ring depth");
         const int later = k == 0 ? kRing - 2 : min(kRing - 2, n_my - 1 - k);
         if (later >= 2)
