@@ -96,24 +96,24 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_092_634, write=73_933, source="int4vh.hip",
-                      source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "full_t8": dict(read=390_418_842, write=41_062, source="int4vh.hip",
-                     source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "two_blocks_t16": dict(read=393_102_541, write=74_035, source="int4vh.hip",
-                            source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "batch": dict(read=684_017_459, write=1_062_195, source="int4vh.hip",
-                   source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "draft_vocab": dict(read=21_349_786, write=17_510, source="int4vh.hip",
-                         source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "shard_t16": dict(read=50_755_994, write=74_957, source="int4vh.hip",
-                       source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "full_t16_top16": dict(read=391_748_403, write=568_525, source="int4vh.hip",
-                            source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "full_t16_top0": dict(read=391_521_280, write=358_912, source="int4vh.hip",
-                           source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
-    "two_blocks_t16_top16": dict(read=393_702_605, write=570_778, source="int4vh.hip",
-                                  source_sha256="d62d3450bbde8c991c168d1d9bcba9ace75a3f29b5ba7ceaa8e13bf21a1977c6"),
+    "full_t16": dict(read=391_106_081, write=73_920, source="int4vh.hip",
+                      source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "full_t8": dict(read=390_428_077, write=41_088, source="int4vh.hip",
+                     source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "two_blocks_t16": dict(read=393_092_283, write=74_048, source="int4vh.hip",
+                            source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "batch": dict(read=684_007_154, write=1_062_176, source="int4vh.hip",
+                   source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "draft_vocab": dict(read=21_341_596, write=17_536, source="int4vh.hip",
+                         source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "shard_t16": dict(read=50_769_449, write=74_944, source="int4vh.hip",
+                       source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "full_t16_top16": dict(read=391_756_697, write=568_576, source="int4vh.hip",
+                            source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "full_t16_top0": dict(read=391_539_208, write=358_912, source="int4vh.hip",
+                           source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+    "two_blocks_t16_top16": dict(read=393_708_850, write=570_816, source="int4vh.hip",
+                                  source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
