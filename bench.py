@@ -97,23 +97,23 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
     "full_t16": dict(read=391_106_081, write=73_920, source="int4vh.hip",
-                      source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                      source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "full_t8": dict(read=390_428_077, write=41_088, source="int4vh.hip",
-                     source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                     source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "two_blocks_t16": dict(read=393_092_283, write=74_048, source="int4vh.hip",
-                            source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                            source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "batch": dict(read=684_007_154, write=1_062_176, source="int4vh.hip",
-                   source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                   source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "draft_vocab": dict(read=21_341_596, write=17_536, source="int4vh.hip",
-                         source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                         source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "shard_t16": dict(read=50_769_449, write=74_944, source="int4vh.hip",
-                       source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                       source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "full_t16_top16": dict(read=391_756_697, write=568_576, source="int4vh.hip",
-                            source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                            source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "full_t16_top0": dict(read=391_539_208, write=358_912, source="int4vh.hip",
-                           source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                           source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "two_blocks_t16_top16": dict(read=393_708_850, write=570_816, source="int4vh.hip",
-                                  source_sha256="3d577177eb5346b674822cd0f167bf43a197491ab693208826fb006aaac0f3f3"),
+                                  source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }

@@ -47,9 +47,11 @@
 //  group gets its own workgroups, one per tile set, and the workgroups of a
 //  set (one per group, 8 blockIdx apart: the same XCD) walk the same tiles
 //  at the same time, so a tile comes from HBM once and from that XCD's L2
-//  for the others.  Per-tile time is bound by the latency of the three-tile
-//  ring, so the call costs about 46 us more per group; above 64 rows the
-//  matrix-core batch kernels below are faster.
+//  for the others.  Each group's workgroup repeats the per-tile compute
+//  (the int8 MFMAs, at the rate the matrix cores sustain under this load,
+//  plus the nibble conversion and the cross-wave reduction), so the call
+//  costs about 46 us more per group; above 64 rows the matrix-core batch
+//  kernels below are faster.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
