@@ -24,7 +24,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA peak, TOP/s
 SINGLE_BLOCK_ROWS = 64         # larger blocks run the MFMA-bound batch kernels
-SAMPLED_MAX_ROWS = 64          # the sampled epilogue takes up to 64 rows (token groups of 16)
+SAMPLED_MAX_ROWS = 4096        # sampled calls: fused into the weight stream up to 64 rows, then
+                               # the batch kernels' logits and a per-row selection
 METRIC = "int4 lm_head verify: weight GB/s (% HBM peak) and verified tokens/s at T=16"
 # what the path computes: int4 weights times 24-bit fixed-point activation
 # codes (x*s, exact in binary32, rounded to 24 bits), run as three int8 MFMA
@@ -572,7 +573,9 @@ def main():
     if args.calibrate_copy:
         calibration_copy(torch, dev)
 
-    work = binding.Workspace(binding.workspace_bytes(cfg.R, cfg.T, cfg.V, cfg.H), dev)
+    # (a sampled call above 64 rows also keeps its logits in the workspace)
+    ws_size = binding.sampled_workspace_bytes if (args.top_k > 0 or args.full_softmax) else binding.workspace_bytes
+    work = binding.Workspace(ws_size(cfg.R, cfg.T, cfg.V, cfg.H), dev)
     stream = torch.cuda.current_stream(dev)
 
     # The draft-vocabulary head: its rows are a subset of the full vocabulary

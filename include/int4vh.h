@@ -109,6 +109,12 @@ enum {
  * invalid).  Pure host function. */
 size_t verify_lm_head_int4_workspace_bytes(int R, int T, int V, int H);
 
+/* Bytes of workspace verify_lm_head_int4_sampled (and its _timed variant)
+ * needs: the same as verify_lm_head_int4_workspace_bytes up to 64 rows; above,
+ * that plus the call's logits, R*T*V*4 bytes (rounded to 256).  0 if the
+ * sizes are invalid.  Pure host function. */
+size_t verify_lm_head_int4_sampled_workspace_bytes(int R, int T, int V, int H);
+
 /* Zero the workspace's control words on `stream` (a small fill kernel, no
  * memset node, so it may be captured in a graph).  Call once after
  * allocation.  Returns INT4VH_EINVAL for NULL, INT4VH_EALIGN if not 256-byte
@@ -194,10 +200,14 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
                                int32_t *n_accepted, float *logits_out, void *workspace,
                                size_t workspace_bytes, void *stream);
 
-/* Sampled (non-greedy) verification: the verify call with a sampling
- * epilogue fused into the same weight stream, for R*T <= 64 rows (R
- * requests of T positions; beyond 16 rows in token groups of 16 sharing the
- * tile stream, like the greedy call).  The int4 head suffices because top-k
+/* Sampled (non-greedy) verification for R*T <= 4096 rows (R requests of T
+ * positions).  Up to 64 rows the sampling epilogue is fused into the weight
+ * stream (beyond 16 rows in token groups of 16 sharing the tile stream, like
+ * the greedy call); above, the batch kernels write the call's logits into the
+ * workspace and one workgroup per row takes its top-k, log-sum-exp and p(d)
+ * from them (same formulas and ties; the workspace is then
+ * verify_lm_head_int4_sampled_workspace_bytes, and V <= 262144).  The int4
+ * head suffices because top-k
  * sampling needs only the ordering of the logits ("HyperQwen: 1,000 tok/s on
  * a Single RTX 3090 Through Aggressive Recurrent-State Speculation",
  * Technical Insight, lm_head paragraph).  Per row r:
@@ -222,9 +232,11 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
  * draft_probs, uniforms, p_draft: device float32 [R, T-1] (may be NULL only
  * when T == 1); topk_ids int32 / topk_logits float32 [R*T, top_k] (may be
  * NULL when top_k == 0); lse float32 [R*T] or NULL.
- * Errors as verify_lm_head_int4_batch, plus INT4VH_EINVAL for top_k outside
- * [0, min(16, V)], a temperature that is not finite and > 0, or a missing
- * sampled buffer, and INT4VH_EUNSUPPORTED for R*T > 64. */
+ * Errors as verify_lm_head_int4_batch (INT4VH_EWORKSPACE against
+ * verify_lm_head_int4_sampled_workspace_bytes), plus INT4VH_EINVAL for top_k
+ * outside [0, min(16, V)], a temperature that is not finite and > 0, or a
+ * missing sampled buffer, and INT4VH_EUNSUPPORTED for R*T > 64 with
+ * V > 262144. */
 int verify_lm_head_int4_sampled(const void *hidden, const uint8_t *packed_w, const void *scales,
                                 const int32_t *draft_ids, const float *draft_probs,
                                 const float *uniforms, int R, int T, int V, int H, int top_k,

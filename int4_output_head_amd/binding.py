@@ -35,6 +35,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         L.verify_lm_head_int4_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.verify_lm_head_int4_workspace_bytes.restype = sz
+        L.verify_lm_head_int4_sampled_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.verify_lm_head_int4_sampled_workspace_bytes.restype = sz
         L.verify_lm_head_int4_workspace_init.argtypes = [P, sz, P]
         L.verify_lm_head_int4_workspace_init.restype = i32
         L.verify_lm_head_int4.argtypes = [P, P, P, P, i32, i32, i32, P, P, P, P, P, sz, P]
@@ -107,6 +109,10 @@ def _stream_ptr(device):
 
 def workspace_bytes(R: int, T: int, V: int, H: int) -> int:
     return int(load_library().verify_lm_head_int4_workspace_bytes(R, T, V, H))
+
+
+def sampled_workspace_bytes(R: int, T: int, V: int, H: int) -> int:
+    return int(load_library().verify_lm_head_int4_sampled_workspace_bytes(R, T, V, H))
 
 
 class Workspace:
@@ -318,7 +324,7 @@ def verify_mapped(hidden, packed_w, scales, vocab_ids, draft_ids=None, *, R: int
 def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, uniforms=None, *,
                    top_k: int, temperature: float = 1.0, R: int | None = None,
                    workspace: Workspace | None = None, events=None, want_lse: bool = False):
-    """Sampled verification for R*T <= 64 rows: top-k sampling at a
+    """Sampled verification for R*T <= 4096 rows: top-k sampling at a
     temperature (top_k >= 1) or sampling over the whole vocabulary
     (top_k == 0).  hidden: float16 [R, T, H] (or [R*T, H] with R); draft_ids
     int32, draft_probs and uniforms float32, each [R, T-1] (None when T == 1).
@@ -327,7 +333,8 @@ def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, u
     top-k outputs are None when top_k == 0; lse, the log-sum-exp of
     logit / temperature over the vocabulary, is None unless want_lse or
     top_k == 0).  events=(before, after) are recorded right around the main
-    verify kernel."""
+    verify kernel.  Above 64 rows the workspace also holds the call's logits
+    (sampled_workspace_bytes)."""
     if hidden.dim() == 3:
         R, T, H = hidden.shape
         hidden = hidden.reshape(R * T, H)
@@ -363,7 +370,7 @@ def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, u
     pdr = torch.empty((R, max(T - 1, 1)), dtype=torch.float32, device=dev)
     nacc = torch.empty(R, dtype=torch.int32, device=dev)
     L = load_library()
-    need = L.verify_lm_head_int4_workspace_bytes(R, T, V, H)
+    need = L.verify_lm_head_int4_sampled_workspace_bytes(R, T, V, H)
     if need == 0:
         _raise(EINVAL, "verify_sampled")
     ws = workspace if workspace is not None else _default_workspace(dev, need)

@@ -2056,6 +2056,289 @@ __global__ void __launch_bounds__(256) count_bad_map(const int32_t *map, int V, 
         atomicAdd(out, cnt);
 }
 
+// ---------------------------------------------------------------- topk_rows_kernel
+// Sampled verification of calls past the weight-stream kernels' 64 rows: the
+// batch kernel writes every logit of the call into the workspace, and one
+// workgroup per row then takes the row's top-k (order keys: larger value,
+// then lower row), the log-sum-exp of logit / tau over the vocabulary and
+// p(d) of the row's draft, with the formulas of the weight-stream kernels'
+// sampled epilogue.  Exact for any input, ties included: pass 1 (one read of
+// the row) keeps each thread's best key over its slice i = tid, tid + 512,
+// ... and the online (max, sum) of exp2 terms; the kTopK-th largest of the
+// 512 slice keys, th, is at most the row's kTopK-th key, and a key of the row
+// that reaches th lies in a slice whose best key reaches th -- kTopK slices
+// -- so pass 2 reads only those slices (spread over all the threads) and
+// gathers at most kTopK * ceil(V / 512) keys into LDS, and the kTopK largest
+// of those are the row's.
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelMaxV = 262144;     // vocabulary rows this path takes: keeps the candidates within LDS
+constexpr int kSelUnroll = 16;       // loads in flight per thread
+
+struct SArgs {
+    const float *logits;      // [M, V] binary32, in the workspace
+    const int32_t *draft;     // [R, T-1] or null
+    int32_t *topk_ids;        // [M, top_k] or null
+    float *topk_logits;       // [M, top_k] or null
+    float *p_draft;           // [R, T-1] or null
+    float *lse_out;           // [M] or null
+    int R, T, V, top_k;
+    float tau;
+};
+
+__device__ __forceinline__ unsigned long long key_shfl_xor(unsigned long long k, int mask)
+{
+    const uint32_t lo = __shfl_xor((uint32_t)k, mask);
+    const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), mask);
+    return ((unsigned long long)hi << 32) | lo;
+}
+
+// The 64 keys of a wave (one per lane), sorted best first across the lanes:
+// a bitonic network of cross-lane compare-exchanges (keys are distinct).
+__device__ __forceinline__ unsigned long long wave_sort64(unsigned long long k, int lane)
+{
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const unsigned long long o = key_shfl_xor(k, stride);
+            // descending overall: the lower lane of a pair keeps the larger key
+            // in blocks whose bit `size` is clear, the smaller one otherwise
+            const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+            k = keep_max ? (o > k ? o : k) : (o < k ? o : k);
+        }
+    return k;
+}
+
+// The best 64 of two best-first lane-sorted lists, best first: the larger of
+// a[j] and b[63 - j] form a bitonic sequence of exactly those 64 keys, which a
+// bitonic merge sorts.
+__device__ __forceinline__ unsigned long long wave_merge64(unsigned long long a, unsigned long long b, int lane)
+{
+    const unsigned long long br = key_shfl(b, 63 - lane);
+    unsigned long long m = a > br ? a : br;
+#pragma unroll
+    for (int stride = 32; stride > 0; stride >>= 1) {
+        const unsigned long long o = key_shfl_xor(m, stride);
+        m = (lane & stride) == 0 ? (o > m ? o : m) : (o < m ? o : m);
+    }
+    return m;
+}
+
+// The kTopK largest of the n distinct keys buf[0, n) into out[0, kTopK), best
+// first (key 0, below every real key, for ranks past n).  Each wave keeps the
+// best 64 of its chunks of 64 keys (sort, merge); wave 0 merges the waves'
+// best kTopK.  Called by the whole workgroup; out is complete when it
+// returns.
+template <int kTopK>
+__device__ void wg_top_keys(const unsigned long long *buf, int n, unsigned long long *out,
+                            unsigned long long (*wtop)[kTopK])
+{
+    static_assert(kSelWaves * kTopK <= 128, "two registers of wave 0 hold the waves' lists");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned long long r = 0ull;
+    for (int c = wave * 64; c < n; c += kSelThreads) {
+        const unsigned long long k = c + lane < n ? buf[c + lane] : 0ull;
+        r = wave_merge64(r, wave_sort64(k, lane), lane);
+    }
+    if (lane < kTopK)
+        wtop[wave][lane] = r;
+    __syncthreads();
+    if (wave == 0) {
+        constexpr int kAll = kSelWaves * kTopK;
+        const unsigned long long a = lane < kAll ? wtop[lane / kTopK][lane % kTopK] : 0ull;
+        unsigned long long m = wave_sort64(a, lane);
+        if constexpr (kAll > 64) {
+            const unsigned long long b = 64 + lane < kAll ? wtop[(64 + lane) / kTopK][(64 + lane) % kTopK] : 0ull;
+            m = wave_merge64(m, wave_sort64(b, lane), lane);
+        }
+        if (lane < kTopK)
+            out[lane] = m;
+    }
+    __syncthreads();
+}
+
+// Grid: one workgroup per row of the call.  kTopK: 8 or 16 (top_k rounded up;
+// 0 for sampling over the whole vocabulary, which needs no list: the greedy
+// outputs come from the batch kernel).  kLse: the log-sum-exp is needed (top_k
+// == 0, or the caller asked for it).
+template <int kTopK, bool kLse>
+__global__ void __launch_bounds__(kSelThreads) topk_rows_kernel(SArgs a)
+{
+    constexpr int kCand = kTopK * (kSelMaxV / kSelThreads);   // gathered keys, at most
+    __shared__ unsigned long long s_cand[kCand > 0 ? kCand : 1];
+    __shared__ unsigned long long s_slice[kSelThreads];
+    __shared__ unsigned long long s_top[kTopK > 0 ? kTopK : 1];
+    __shared__ unsigned long long s_wtop[kSelWaves][kTopK > 0 ? kTopK : 1];
+    __shared__ float s_lm[kSelWaves], s_ls[kSelWaves];
+    __shared__ int s_qs[kTopK > 0 ? kTopK : 1];
+    __shared__ int s_n, s_nq;
+
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int V = a.V;
+    const float *lg = a.logits + (size_t)m * V;
+    const float zscale = 1.4426950408889634f / a.tau;   // log2(e) / tau
+
+    // pass 1: the slice's best key (strict >: the first of its largest
+    // values, i.e. the lowest row; -0.0 and +0.0 tie) and its (max, sum) of
+    // exp2(logit * log2(e) / tau), one exp2 per logit
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7FFFFFFF;
+    float lm = -__builtin_huge_valf(), ls = 0.0f;
+    auto take = [&](float v, int i) {
+        if constexpr (kTopK > 0) {
+            bi = v > bv ? i : bi;
+            bv = v > bv ? v : bv;
+        }
+        if constexpr (kLse) {
+            const float z = v * zscale;
+            const float mn = fmaxf(lm, z);
+            const float e = __builtin_amdgcn_exp2f(fminf(lm, z) - mn);   // exp2 of (smaller - larger)
+            ls = z > lm ? ls * e + 1.0f : ls + e;
+            lm = mn;
+        }
+    };
+    // kSelUnroll loads in flight per thread (the row comes from memory), then
+    // their values in order of the row
+    int i0 = tid;
+    for (; i0 + (kSelUnroll - 1) * kSelThreads < V; i0 += kSelUnroll * kSelThreads) {
+        float v[kSelUnroll];
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u)
+            v[u] = lg[i0 + u * kSelThreads];
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u)
+            take(v[u], i0 + u * kSelThreads);
+    }
+    for (; i0 < V; i0 += kSelThreads)
+        take(lg[i0], i0);
+    if constexpr (kLse) {
+        row_lse16(lm, ls);
+        lse_combine(lm, ls, __shfl_xor(lm, 16), __shfl_xor(ls, 16));
+        lse_combine(lm, ls, __shfl_xor(lm, 32), __shfl_xor(ls, 32));
+        if (lane == 0) {
+            s_lm[wave] = lm;
+            s_ls[wave] = ls;
+        }
+    }
+    if constexpr (kTopK > 0) {
+        // a thread past the row keeps (-inf, 0x7FFFFFFF): below every logit's key
+        s_slice[tid] = order_key(bv, bi);
+        if (tid == 0) {
+            s_n = 0;
+            s_nq = 0;
+        }
+        __syncthreads();
+        wg_top_keys<kTopK>(s_slice, kSelThreads, s_top, s_wtop);
+        // th is 0 when the row has fewer than kTopK logits (the slices past it
+        // share one key): then every logit is a candidate
+        const unsigned long long th = s_top[kTopK - 1];
+        const float thv = th != 0ull ? key_value(th) : -__builtin_huge_valf();
+        // the slices that can hold a key reaching th: those whose best key
+        // does (at most kTopK; every slice of a row shorter than kTopK)
+        if (tid < V && s_slice[tid] >= th) {
+            const int slot = atomicAdd(&s_nq, 1);
+            if (slot < kTopK)
+                s_qs[slot] = tid;
+        }
+        __syncthreads();
+        // pass 2: their keys that reach th, the slices' elements spread over
+        // every thread (all of a thread's loads in flight at once; value test
+        // first, a key reaching th has a value reaching th's)
+        const int nq = min(s_nq, kTopK);
+        const int len = (V + kSelThreads - 1) / kSelThreads;    // elements of a slice, at most
+        const int n_el = nq * len;
+        for (int e0 = tid; e0 < n_el; e0 += kSelUnroll * kSelThreads) {
+            float v[kSelUnroll];
+            int idx[kSelUnroll];
+#pragma unroll
+            for (int u = 0; u < kSelUnroll; ++u) {
+                const int e = e0 + u * kSelThreads;
+                const int q = e / len;
+                const int i = e < n_el ? s_qs[q] + (e - q * len) * kSelThreads : V;
+                idx[u] = i < V ? i : -1;
+                v[u] = i < V ? lg[i] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kSelUnroll; ++u) {
+                if (idx[u] >= 0 && v[u] >= thv) {
+                    const unsigned long long k = order_key(v[u], idx[u]);
+                    if (k >= th) {
+                        const int slot = atomicAdd(&s_n, 1);
+                        if (slot < kCand)
+                            s_cand[slot] = k;
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        wg_top_keys<kTopK>(s_cand, min(s_n, kCand), s_top, s_wtop);
+    } else {
+        __syncthreads();
+    }
+
+    // outputs: wave 0, lane j of its first 16 lanes takes rank j
+    if (wave != 0)
+        return;
+    const int T = a.T, req = m / T, t = m % T;
+    const bool drafted = t < T - 1;
+    const int di = drafted ? req * (T - 1) + t : 0;
+    const int d = drafted ? a.draft[di] : -1;
+    float lse = 0.0f;
+    if constexpr (kLse) {
+        float gm = s_lm[0], gs = s_ls[0];
+#pragma unroll
+        for (int w = 1; w < kSelWaves; ++w)
+            lse_combine(gm, gs, s_lm[w], s_ls[w]);
+        lse = (gm + __log2f(gs)) * 0.6931471805599453f;
+    }
+    float p = 0.0f;
+    if constexpr (kTopK > 0) {
+        const int j = lane & 15;
+        const unsigned long long key = j < kTopK ? s_top[j] : 0ull;
+        const float hv = key_value(key);
+        const int hi = key_index(key);
+        const float lmax = key_value(s_top[0]);
+        const bool in = lane < 16 && j < a.top_k;
+        const float e = in ? expf((hv - lmax) / a.tau) : 0.0f;
+        const float sum = row_sum16(e);
+        const float e_d = row_sum16(in && hi == d ? e : 0.0f);
+        if (in) {
+            a.topk_ids[(size_t)m * a.top_k + j] = hi;
+            a.topk_logits[(size_t)m * a.top_k + j] = hv;
+        }
+        p = e_d / sum;
+    } else {
+        p = (d >= 0 && d < V) ? expf(lg[d] / a.tau - lse) : 0.0f;
+    }
+    if (lane == 0) {
+        if (kLse && a.lse_out)
+            a.lse_out[m] = lse;
+        if (drafted)
+            a.p_draft[di] = p;
+    }
+}
+
+// The accepted count of each request from its rows' p(d): drafts are
+// accepted while uniforms * draft_probs < p_draft (binary32, the comparison of
+// the weight-stream kernels' epilogue).
+__global__ void __launch_bounds__(256) accept_rows_kernel(const float *p_draft, const float *dprob, const float *unif,
+                                                          int R, int T, int32_t *n_acc)
+{
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= R)
+        return;
+    int n = 0;
+    while (n < T - 1) {
+        const int di = i * (T - 1) + n;
+        if (!(unif[di] * dprob[di] < p_draft[di]))
+            break;
+        ++n;
+    }
+    n_acc[i] = n;
+}
+
 // ---------------------------------------------------------------- host side
 
 int hip_fail(hipError_t e, const char *what)
@@ -2239,6 +2522,20 @@ size_t workspace_need(int R, int T, int V, int H)
         return sampled_base((int)((M + kMaxRows - 1) / kMaxRows)) + kSampledArea;
     const size_t n_mt = (size_t)((M + kRTokTile - 1) / kRTokTile);
     return kWsFrag + n_mt * (size_t)kRTbPerTile * (size_t)rows_steps(H) * 2 * 3 * 64 * 16;
+}
+
+// The sampled call's workspace: past the weight-stream kernels' rows the
+// call's logits (binary32 [M, V]) follow the batch path's area.
+size_t logits_offset(int R, int T, int V, int H)
+{
+    return (workspace_need(R, T, V, H) + 255) & ~(size_t)255;
+}
+size_t sampled_need(int R, int T, int V, int H)
+{
+    const size_t base = workspace_need(R, T, V, H);
+    if (base == 0 || (long long)R * T <= kStreamMaxRows)
+        return base;
+    return logits_offset(R, T, V, H) + (size_t)R * (size_t)T * (size_t)V * sizeof(float);
 }
 
 // Every argument check except the workspace's (no GPU call).
@@ -2478,6 +2775,62 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
     return record_event(ev1, s, "event record after verify kernel");
 }
 
+// Sampled call of more than 64 rows: the batch kernels with the logits
+// written to the workspace, then topk_rows_kernel (one workgroup per row) and
+// the acceptance count.
+int launch_sampled_rows(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
+                        int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
+                        void *ws, size_t ws_bytes, void *stream, void *ev0, void *ev1, const Sampled &smp)
+{
+    int st = validate_args(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, nullptr);
+    if (st != INT4VH_OK)
+        return st;
+    if (!ws)
+        return INT4VH_EINVAL;
+    if (!aligned(ws, 256))
+        return INT4VH_EALIGN;
+    if (V > kSelMaxV)
+        return INT4VH_EUNSUPPORTED;
+    if (ws_bytes < sampled_need(R, T, V, H))
+        return INT4VH_EWORKSPACE;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "hipGetDevice");
+    char *wsb = static_cast<char *>(ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    float *lg = reinterpret_cast<float *>(wsb + logits_offset(R, T, V, H));
+    st = launch_rows(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lg, nullptr, wsb, dev, s, ev0,
+                     ev1);
+    if (st != INT4VH_OK)
+        return st;
+    const SArgs a{lg, draft, smp.topk_ids, smp.topk_logits, smp.p_draft, smp.lse, R, T, V, smp.top_k, smp.tau};
+    const bool lse = smp.top_k == 0 || smp.lse != nullptr;
+    const dim3 grid(R * T), block(kSelThreads);
+    if (smp.top_k == 0)
+        hipLaunchKernelGGL((topk_rows_kernel<0, true>), grid, block, 0, s, a);
+    else if (smp.top_k <= 8 && lse)
+        hipLaunchKernelGGL((topk_rows_kernel<8, true>), grid, block, 0, s, a);
+    else if (smp.top_k <= 8)
+        hipLaunchKernelGGL((topk_rows_kernel<8, false>), grid, block, 0, s, a);
+    else if (lse)
+        hipLaunchKernelGGL((topk_rows_kernel<16, true>), grid, block, 0, s, a);
+    else
+        hipLaunchKernelGGL((topk_rows_kernel<16, false>), grid, block, 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return hip_fail(e, "topk_rows kernel launch");
+    if (T > 1) {
+        // (the batch kernel's greedy count is replaced)
+        hipLaunchKernelGGL(accept_rows_kernel, dim3((R + 255) / 256), dim3(256), 0, s, smp.p_draft, smp.dprob,
+                           smp.unif, R, T, nacc);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return hip_fail(e, "accept_rows kernel launch");
+    }
+    return INT4VH_OK;
+}
+
 // ---------------------------------------------------------------- static scratch
 // The workspace of verify_lm_head_int4_batch_noalloc: one array per device,
 // allocated when the code object is loaded and held until the process ends.
@@ -2541,6 +2894,11 @@ extern "C" {
 size_t verify_lm_head_int4_workspace_bytes(int R, int T, int V, int H)
 {
     return workspace_need(R, T, V, H);
+}
+
+size_t verify_lm_head_int4_sampled_workspace_bytes(int R, int T, int V, int H)
+{
+    return sampled_need(R, T, V, H);
 }
 
 int verify_lm_head_int4_workspace_init(void *ws, size_t ws_bytes, void *stream)
@@ -2651,9 +3009,10 @@ int verify_lm_head_int4_sampled_timed(const void *hidden, const uint8_t *packed_
         (lse && !aligned(lse, 4)) || (draft_probs && !aligned(draft_probs, 4)) ||
         (uniforms && !aligned(uniforms, 4)) || (p_draft && !aligned(p_draft, 4)))
         return INT4VH_EALIGN;
-    // (more than 16 rows: INT4VH_EUNSUPPORTED from launch_verify, after the
-    // common validation)
     const Sampled smp{top_k, temperature, draft_probs, uniforms, topk_ids, topk_logits, p_draft, lse};
+    if (R >= 1 && T >= 1 && (long long)R * T > kStreamMaxRows)
+        return launch_sampled_rows(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
+                                   n_accepted, workspace, workspace_bytes, stream, event_before, event_after, smp);
     return launch_verify(hidden, packed_w, scales, draft_ids, R, T, V, H, logits_max, argmax_ids,
                          n_accepted, nullptr, workspace, workspace_bytes, stream, event_before,
                          event_after, nullptr, &smp);

@@ -35,6 +35,8 @@ def lib():
     L.verify_lm_head_int4_batch.argtypes = [P, P, P, P, i32, i32, i32, i32, P, P, P, P, P, sz, P]
     L.verify_lm_head_int4_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.verify_lm_head_int4_workspace_bytes.restype = sz
+    L.verify_lm_head_int4_sampled_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.verify_lm_head_int4_sampled_workspace_bytes.restype = sz
     L.verify_lm_head_int4_workspace_init.argtypes = [P, sz, P]
     L.verify_lm_head_int4_check_weights.argtypes = [P, i32, i32, P, P]
     L.verify_lm_head_int4_status_string.argtypes = [i32]
@@ -50,7 +52,7 @@ def test_header_declares_expected_api():
               "verify_lm_head_int4_check_weights", "verify_lm_head_int4_status_string",
               "verify_lm_head_int4_last_error", "verify_lm_head_int4_mapped",
               "verify_lm_head_int4_check_vocab_map", "verify_lm_head_int4_sampled",
-              "verify_lm_head_int4_sampled_timed",
+              "verify_lm_head_int4_sampled_timed", "verify_lm_head_int4_sampled_workspace_bytes",
               "context_copy_propose", "context_copy_propose_timed",
               "requant_lm_head_int4_amax",
               "requant_lm_head_int4_scales", "requant_lm_head_int4_pack",
@@ -79,6 +81,22 @@ def test_workspace_bytes(lib):
     assert lib.verify_lm_head_int4_workspace_bytes(1, 17, 10, 64) == 0
     assert lib.verify_lm_head_int4_workspace_bytes(1, 4, 0, 64) == 0
     assert lib.verify_lm_head_int4_workspace_bytes(1, 4, 10, 48) == 0
+
+
+def test_sampled_workspace_bytes(lib):
+    g = lib.verify_lm_head_int4_workspace_bytes
+    f = lib.verify_lm_head_int4_sampled_workspace_bytes
+    # up to 64 rows the sampled epilogue rides on the weight stream: same workspace
+    for R, T in ((1, 16), (4, 16), (3, 7)):
+        assert f(R, T, 151936, 5120) == g(R, T, 151936, 5120) > 0
+    # above, the call's logits follow the batch area (256-byte aligned)
+    for R, T, V in ((5, 13, 100), (64, 4, 151936), (256, 16, 8192)):
+        base = g(R, T, V, 5120)
+        assert base > 0
+        assert f(R, T, V, 5120) == (base + 255) // 256 * 256 + R * T * V * 4
+    assert f(1, 0, 10, 64) == 0
+    assert f(257, 16, 10, 64) == 0                    # more than 4096 rows
+    assert f(1, 4, 10, 48) == 0
 
 
 A = 0x10000          # a fake, 256-byte aligned "device pointer" (never dereferenced)
@@ -227,7 +245,11 @@ def test_sampled_rejects_invalid_arguments(lib):
     assert scall(pdr=0) == EINVAL
     assert scall(tids=0) == EINVAL
     assert scall(tlog=A + 2) == EALIGN
-    assert scall(R=5, T=13) == EUNSUPPORTED           # more than 64 rows
+    # more than 64 rows: the batch path, whose workspace also holds the logits
+    # and which takes vocabularies up to 262144 rows
+    assert scall(R=5, T=13, ws_bytes=lib.verify_lm_head_int4_workspace_bytes(5, 13, 100, 256)) == EWORKSPACE
+    assert scall(R=5, T=13, V=262145) == EUNSUPPORTED
+    assert scall(R=257, T=16) == EINVAL               # more than 4096 rows
     assert scall(R=1, T=17) == EINVAL
     assert scall(ws_bytes=100) == EWORKSPACE
 

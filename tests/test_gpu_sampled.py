@@ -216,7 +216,13 @@ def check(g, o, lg, d, q, u, R, T, k, tau):
                                            # more than 16 rows: token groups of 16
                                            (2, 16, 5000, 512, 16, 1.0), (3, 11, 4097, 256, 8, 0.7),
                                            (4, 16, 3000, 128, 16, 1.3), (17, 1, 2000, 96, 5, 2.0),
-                                           (5, 12, 20000, 1024, 16, 0.3)])
+                                           (5, 12, 20000, 1024, 16, 0.3),
+                                           # more than 64 rows: the batch kernels' logits and
+                                           # the per-row selection
+                                           (9, 8, 5000, 512, 16, 1.0), (33, 4, 4097, 256, 8, 0.7),
+                                           (65, 1, 2000, 96, 5, 2.0), (16, 16, 3000, 128, 16, 0.3),
+                                           (100, 3, 600, 64, 12, 1.3), (8, 10, 300, 64, 16, 1.0),
+                                           (13, 5, 12, 64, 12, 1.0)])
 def test_sampled_parity(vh, oracle_mod, R, T, V, H, k, tau):
     say(f"sampled R={R} T={T} V={V} H={H} k={k} tau={tau}")
     inp = synth.uniform_inputs(R * T, V, H, seed=R * 31 + T + V + H + k)
@@ -266,7 +272,10 @@ def check_full_softmax(g, o, lg, d, q, u, R, T, tau):
                                          (4, 4, 999, 96, 2.0), (1, 8, 151936, 5120, 1.0),
                                          (1, 16, 20000, 1024, 0.7), (2, 4, 3000, 256, 1.3),
                                          (2, 16, 5000, 512, 1.0), (4, 16, 3000, 256, 0.7),
-                                         (3, 7, 4097, 96, 2.0)])
+                                         (3, 7, 4097, 96, 2.0),
+                                         # more than 64 rows
+                                         (9, 8, 5000, 512, 1.0), (40, 4, 4097, 256, 0.7),
+                                         (33, 2, 20000, 1024, 2.0)])
 def test_full_softmax_parity(vh, oracle_mod, R, T, V, H, tau):
     """Sampling over the whole vocabulary (top_k = 0): the fused online
     log-sum-exp and the draft's probability against the oracle."""
@@ -330,11 +339,12 @@ def test_sampled_full_vocab_t16(vh, oracle_mod):
     say(f"full-vocab T=16 stats {st}")
 
 
-@pytest.mark.parametrize("R,T", [(2, 8), (3, 16)])
+@pytest.mark.parametrize("R,T", [(2, 8), (3, 16), (9, 8), (20, 4)])
 def test_sampled_int_exact_bitexact(vh, oracle_mod, R, T):
     """Integer-exact inputs: the top-k ids (ties broken by the lowest row
     across tiles and workgroups) and logits equal the oracle's bit for bit
-    (one block of 16 rows, and three token groups)."""
+    (one block of 16 rows, three token groups, and beyond 64 rows the
+    per-row selection over the batch kernels' logits)."""
     V, H, k = 3000, 512, 16
     inp = synth.int_exact_inputs(R * T, V, H, seed=12)
     lg = oracle_mod.logits(inp["hidden"], inp["packed"], inp["scales"], R * T, V, H)
@@ -395,11 +405,11 @@ def test_k1_is_greedy_acceptance(vh):
     assert torch.all(out[4][0, :9] == 1.0) and float(out[4][0, 9]) == 0.0
 
 
-@pytest.mark.parametrize("R,T", [(1, 8), (3, 12)])
+@pytest.mark.parametrize("R,T", [(1, 8), (3, 12), (20, 4)])
 def test_sampled_then_greedy_workspace_reuse(vh, R, T):
     """Sampled and greedy calls alternate on one workspace; each call leaves
-    it ready for the next (results equal fresh calls), with one block and
-    with token groups."""
+    it ready for the next (results equal fresh calls), with one block, with
+    token groups and with the batch path."""
     V, H = 6000, 256
     inp = synth.uniform_inputs(R * T, V, H, seed=5 + R)
     x = dev(inp["hidden"], torch.float16).reshape(R, T, H)
@@ -408,7 +418,7 @@ def test_sampled_then_greedy_workspace_reuse(vh, R, T):
     d = dev((np.arange(R * (T - 1), dtype=np.int32) % V).reshape(R, T - 1))
     q = torch.ones((R, T - 1), dtype=torch.float32, device="cuda")
     u = torch.rand((R, T - 1), dtype=torch.float32, device="cuda")
-    ws = vh.Workspace(vh.workspace_bytes(R, T, V, H), x.device)
+    ws = vh.Workspace(vh.sampled_workspace_bytes(R, T, V, H), x.device)
     a1 = vh.verify_sampled(x, w, s, d, q, u, top_k=16, workspace=ws)
     b1 = vh.verify_batch(x, w, s, d, workspace=ws)
     a2 = vh.verify_sampled(x, w, s, d, q, u, top_k=16, workspace=ws)
@@ -418,3 +428,38 @@ def test_sampled_then_greedy_workspace_reuse(vh, R, T):
         assert (p1 is None and p2 is None) or torch.equal(p1, p2)
     for p1, p2 in zip(b1, b2):
         assert torch.equal(p1, p2)
+
+
+def test_batch_sampled_crowded_slice(vh, oracle_mod):
+    """More than 64 rows, integer-exact logits built so that each row's
+    largest values all sit in one thread's slice of the row selection (rows
+    v = c0, c0 + 512, ...) and tie with each other and with a crowd of
+    second-largest values: the candidates come from few slices and the order
+    falls to the lowest rows.  Top-k ids and logits equal the oracle's bit
+    for bit, and p(d) the oracle's formula on them."""
+    R, T, V, H, k = 33, 2, 10000, 64, 16
+    M = R * T
+    say(f"crowded slice R={R} T={T} V={V} H={H} k={k}")
+    inp = synth.int_exact_inputs(M, V, H, seed=21)
+    q = inp["q"].copy()
+    rng = np.random.default_rng(5)
+    rows = np.arange(V)
+    for c in range(H):
+        q[:, c] = rng.integers(-7, 6, size=V)             # below the two top values
+        q[rows % 3 == c % 3, c] = 6                        # a crowd of second-largest values
+        q[rows % 512 == (7 * c) % 512, c] = 7              # the largest: one slice of 512
+    x = np.zeros((M, H))
+    x[np.arange(M), np.arange(M) % H] = 1.0                # row m reads channel m % H
+    inp = dict(hidden=synth.f16_bits(x), packed=synth.pack_int4(q), scales=inp["scales"])
+    lg = oracle_mod.logits(inp["hidden"], inp["packed"], inp["scales"], M, V, H)
+    d, qd, u = make_drafts(lg, R, T, k, seed=6)
+    o = sm.verify_sampled(inp["hidden"], inp["packed"], inp["scales"], d, qd, u, R, T, V, H, k, 1.0)
+    g = run(vh, inp, d, qd, u, R, T, V, H, k, 1.0)
+    assert np.array_equal(g["topk_ids"], o["topk_ids"])
+    assert np.array_equal(g["topk_logits"], o["topk_logits"])
+    for m in range(M):                                 # the 16 best are the slice's first 16 rows
+        c0 = (7 * (m % H)) % 512
+        assert np.array_equal(g["topk_ids"][m], c0 + 512 * np.arange(16)), m
+    assert np.allclose(g["p_draft"], o["p_draft"], rtol=1e-5, atol=1e-7)
+    check(g, o, lg, d, qd, u, R, T, k, 1.0)
+    check_own_logits(g, d, R, T, k, 1.0)
