@@ -111,8 +111,9 @@ size_t verify_lm_head_int4_workspace_bytes(int R, int T, int V, int H);
 
 /* Bytes of workspace verify_lm_head_int4_sampled (and its _timed variant)
  * needs: the same as verify_lm_head_int4_workspace_bytes up to 64 rows; above,
- * that plus the call's logits, R*T*V*4 bytes (rounded to 256).  0 if the
- * sizes are invalid.  Pure host function. */
+ * that plus the call's logits, R*T*V*4 bytes, and the rows' best keys per
+ * vocabulary tile of 128 rows, R*T*ceil(V/128)*8 bytes (areas rounded to
+ * 256).  0 if the sizes are invalid.  Pure host function. */
 size_t verify_lm_head_int4_sampled_workspace_bytes(int R, int T, int V, int H);
 
 /* Zero the workspace's control words on `stream` (a small fill kernel, no
@@ -206,8 +207,8 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
  * the greedy call); above, the batch kernels write the call's logits into the
  * workspace and one workgroup per row takes its top-k, log-sum-exp and p(d)
  * from them (same formulas and ties; the workspace is then
- * verify_lm_head_int4_sampled_workspace_bytes, and V <= 262144).  The int4
- * head suffices because top-k
+ * verify_lm_head_int4_sampled_workspace_bytes).  The int4 head suffices
+ * because top-k
  * sampling needs only the ordering of the logits ("HyperQwen: 1,000 tok/s on
  * a Single RTX 3090 Through Aggressive Recurrent-State Speculation",
  * Technical Insight, lm_head paragraph).  Per row r:
@@ -235,8 +236,7 @@ int verify_lm_head_int4_mapped(const void *hidden, const uint8_t *packed_w, cons
  * Errors as verify_lm_head_int4_batch (INT4VH_EWORKSPACE against
  * verify_lm_head_int4_sampled_workspace_bytes), plus INT4VH_EINVAL for top_k
  * outside [0, min(16, V)], a temperature that is not finite and > 0, or a
- * missing sampled buffer, and INT4VH_EUNSUPPORTED for R*T > 64 with
- * V > 262144. */
+ * missing sampled buffer. */
 int verify_lm_head_int4_sampled(const void *hidden, const uint8_t *packed_w, const void *scales,
                                 const int32_t *draft_ids, const float *draft_probs,
                                 const float *uniforms, int R, int T, int V, int H, int top_k,

@@ -505,6 +505,15 @@ __device__ __forceinline__ void lse_combine(float &m, float &s, float mo, float 
     m = mn;
 }
 
+// Adds one term exp2(z) to a running (m, s) pair: one exp2.
+__device__ __forceinline__ void lse_add(float &m, float &s, float z)
+{
+    const float mn = fmaxf(m, z);
+    const float e = __builtin_amdgcn_exp2f(fminf(m, z) - mn);   // exp2 of (smaller - larger)
+    s = z > m ? s * e + 1.0f : s + e;
+    m = mn;
+}
+
 __device__ __forceinline__ uint64_t lse_pack(float m, float s)
 {
     return ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)__float_as_uint(m);
@@ -1628,6 +1637,7 @@ struct RArgs {
     int32_t *argmax;          // [M]
     int32_t *n_acc;           // [R]
     float *logits_out;        // [M, V] or null
+    unsigned long long *item_keys;   // [M, ceil(V / 128)] each row's best key per vocabulary tile, or null
     const int32_t *vmap;      // [V] token id of each head row, or null (identity)
     unsigned long long *keys; // [M] per-token winner keys, zero between calls
     uint32_t *ticket;
@@ -1880,6 +1890,8 @@ __global__ void __launch_bounds__(kRThreads) verify_rows_kernel(RArgs a)
                 }
                 row_best16(bv, bi);
                 const unsigned long long key = order_key(ldexpf(bv, e), bi);
+                if (kLogits && a.item_keys && n16 == 0 && tok < a.M)
+                    a.item_keys[(size_t)tok * ((a.V + kRVocTile - 1) / kRVocTile) + it / n_mt] = key;
                 run[t][r] = key > run[t][r] ? key : run[t][r];
                 if (flush) {
                     if (n16 == 0 && tok < a.M)
@@ -2058,25 +2070,26 @@ __global__ void __launch_bounds__(256) count_bad_map(const int32_t *map, int V, 
 
 // ---------------------------------------------------------------- topk_rows_kernel
 // Sampled verification of calls past the weight-stream kernels' 64 rows: the
-// batch kernel writes every logit of the call into the workspace, and one
-// workgroup per row then takes the row's top-k (order keys: larger value,
-// then lower row), the log-sum-exp of logit / tau over the vocabulary and
-// p(d) of the row's draft, with the formulas of the weight-stream kernels'
-// sampled epilogue.  Exact for any input, ties included: pass 1 (one read of
-// the row) keeps each thread's best key over its slice i = tid, tid + 512,
-// ... and the online (max, sum) of exp2 terms; the kTopK-th largest of the
-// 512 slice keys, th, is at most the row's kTopK-th key, and a key of the row
-// that reaches th lies in a slice whose best key reaches th -- kTopK slices
-// -- so pass 2 reads only those slices (spread over all the threads) and
-// gathers at most kTopK * ceil(V / 512) keys into LDS, and the kTopK largest
-// of those are the row's.
+// batch kernel writes every logit of the call into the workspace, and with it
+// each row's best key over every vocabulary tile of 128 rows (one work item's
+// columns); one workgroup per row then takes the row's top-k (order keys:
+// larger value, then lower row), the log-sum-exp of logit / tau over the
+// vocabulary and p(d) of the row's draft, with the formulas of the
+// weight-stream kernels' sampled epilogue.  Exact for any input, ties
+// included: the kTopK-th largest of the row's tile keys, th, is at most the
+// row's kTopK-th key, and a key of the row that reaches th lies in a tile
+// whose best key reaches th -- kTopK tiles -- so the kernel reads only those
+// tiles' logits (at most kTopK * 128) and the kTopK largest of their keys that
+// reach th are the row's.  The log-sum-exp, when needed, is one read of the
+// whole row (one exp2 per logit).
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kSelMaxV = 262144;     // vocabulary rows this path takes: keeps the candidates within LDS
-constexpr int kSelUnroll = 16;       // loads in flight per thread
+constexpr int kSelTile = 128;        // vocabulary rows per tile key (the batch kernel's work items)
+constexpr int kSelUnroll = 16;       // loads in flight per thread (the log-sum-exp's read of the row)
 
 struct SArgs {
     const float *logits;      // [M, V] binary32, in the workspace
+    const unsigned long long *item_keys;   // [M, ceil(V / 128)] the rows' best keys per tile
     const int32_t *draft;     // [R, T-1] or null
     int32_t *topk_ids;        // [M, top_k] or null
     float *topk_logits;       // [M, top_k] or null
@@ -2165,9 +2178,8 @@ __device__ void wg_top_keys(const unsigned long long *buf, int n, unsigned long 
 template <int kTopK, bool kLse>
 __global__ void __launch_bounds__(kSelThreads) topk_rows_kernel(SArgs a)
 {
-    constexpr int kCand = kTopK * (kSelMaxV / kSelThreads);   // gathered keys, at most
+    constexpr int kCand = kTopK * kSelTile;   // gathered keys, at most
     __shared__ unsigned long long s_cand[kCand > 0 ? kCand : 1];
-    __shared__ unsigned long long s_slice[kSelThreads];
     __shared__ unsigned long long s_top[kTopK > 0 ? kTopK : 1];
     __shared__ unsigned long long s_wtop[kSelWaves][kTopK > 0 ? kTopK : 1];
     __shared__ float s_lm[kSelWaves], s_ls[kSelWaves];
@@ -2178,42 +2190,28 @@ __global__ void __launch_bounds__(kSelThreads) topk_rows_kernel(SArgs a)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int V = a.V;
     const float *lg = a.logits + (size_t)m * V;
-    const float zscale = 1.4426950408889634f / a.tau;   // log2(e) / tau
 
-    // pass 1: the slice's best key (strict >: the first of its largest
-    // values, i.e. the lowest row; -0.0 and +0.0 tie) and its (max, sum) of
-    // exp2(logit * log2(e) / tau), one exp2 per logit
-    float bv = -__builtin_huge_valf();
-    int bi = 0x7FFFFFFF;
-    float lm = -__builtin_huge_valf(), ls = 0.0f;
-    auto take = [&](float v, int i) {
-        if constexpr (kTopK > 0) {
-            bi = v > bv ? i : bi;
-            bv = v > bv ? v : bv;
-        }
-        if constexpr (kLse) {
-            const float z = v * zscale;
-            const float mn = fmaxf(lm, z);
-            const float e = __builtin_amdgcn_exp2f(fminf(lm, z) - mn);   // exp2 of (smaller - larger)
-            ls = z > lm ? ls * e + 1.0f : ls + e;
-            lm = mn;
-        }
-    };
-    // kSelUnroll loads in flight per thread (the row comes from memory), then
-    // their values in order of the row
-    int i0 = tid;
-    for (; i0 + (kSelUnroll - 1) * kSelThreads < V; i0 += kSelUnroll * kSelThreads) {
-        float v[kSelUnroll];
-#pragma unroll
-        for (int u = 0; u < kSelUnroll; ++u)
-            v[u] = lg[i0 + u * kSelThreads];
-#pragma unroll
-        for (int u = 0; u < kSelUnroll; ++u)
-            take(v[u], i0 + u * kSelThreads);
+    if (tid == 0) {
+        s_n = 0;
+        s_nq = 0;
     }
-    for (; i0 < V; i0 += kSelThreads)
-        take(lg[i0], i0);
     if constexpr (kLse) {
+        // (max, sum) of exp2(logit * log2(e) / tau) over the row, one exp2
+        // per logit, kSelUnroll loads in flight per thread
+        const float zscale = 1.4426950408889634f / a.tau;   // log2(e) / tau
+        float lm = -__builtin_huge_valf(), ls = 0.0f;
+        int i0 = tid;
+        for (; i0 + (kSelUnroll - 1) * kSelThreads < V; i0 += kSelUnroll * kSelThreads) {
+            float v[kSelUnroll];
+#pragma unroll
+            for (int u = 0; u < kSelUnroll; ++u)
+                v[u] = lg[i0 + u * kSelThreads];
+#pragma unroll
+            for (int u = 0; u < kSelUnroll; ++u)
+                lse_add(lm, ls, v[u] * zscale);
+        }
+        for (; i0 < V; i0 += kSelThreads)
+            lse_add(lm, ls, lg[i0] * zscale);
         row_lse16(lm, ls);
         lse_combine(lm, ls, __shfl_xor(lm, 16), __shfl_xor(ls, 16));
         lse_combine(lm, ls, __shfl_xor(lm, 32), __shfl_xor(ls, 32));
@@ -2222,60 +2220,49 @@ __global__ void __launch_bounds__(kSelThreads) topk_rows_kernel(SArgs a)
             s_ls[wave] = ls;
         }
     }
+    __syncthreads();
     if constexpr (kTopK > 0) {
-        // a thread past the row keeps (-inf, 0x7FFFFFFF): below every logit's key
-        s_slice[tid] = order_key(bv, bi);
-        if (tid == 0) {
-            s_n = 0;
-            s_nq = 0;
-        }
-        __syncthreads();
-        wg_top_keys<kTopK>(s_slice, kSelThreads, s_top, s_wtop);
-        // th is 0 when the row has fewer than kTopK logits (the slices past it
-        // share one key): then every logit is a candidate
+        const int n_t = (V + kSelTile - 1) / kSelTile;
+        const unsigned long long *tk = a.item_keys + (size_t)m * n_t;
+        wg_top_keys<kTopK>(tk, n_t, s_top, s_wtop);
+        // th is 0 when the row has fewer than kTopK tiles: then every tile
+        // qualifies and every logit is a candidate
         const unsigned long long th = s_top[kTopK - 1];
         const float thv = th != 0ull ? key_value(th) : -__builtin_huge_valf();
-        // the slices that can hold a key reaching th: those whose best key
-        // does (at most kTopK; every slice of a row shorter than kTopK)
-        if (tid < V && s_slice[tid] >= th) {
-            const int slot = atomicAdd(&s_nq, 1);
-            if (slot < kTopK)
-                s_qs[slot] = tid;
-        }
-        __syncthreads();
-        // pass 2: their keys that reach th, the slices' elements spread over
-        // every thread (all of a thread's loads in flight at once; value test
-        // first, a key reaching th has a value reaching th's)
-        const int nq = min(s_nq, kTopK);
-        const int len = (V + kSelThreads - 1) / kSelThreads;    // elements of a slice, at most
-        const int n_el = nq * len;
-        for (int e0 = tid; e0 < n_el; e0 += kSelUnroll * kSelThreads) {
-            float v[kSelUnroll];
-            int idx[kSelUnroll];
-#pragma unroll
-            for (int u = 0; u < kSelUnroll; ++u) {
-                const int e = e0 + u * kSelThreads;
-                const int q = e / len;
-                const int i = e < n_el ? s_qs[q] + (e - q * len) * kSelThreads : V;
-                idx[u] = i < V ? i : -1;
-                v[u] = i < V ? lg[i] : 0.0f;
+        // the tiles whose best key reaches th (at most kTopK)
+        for (int t = tid; t < n_t; t += kSelThreads)
+            if (tk[t] >= th) {
+                const int slot = atomicAdd(&s_nq, 1);
+                if (slot < kTopK)
+                    s_qs[slot] = t;
             }
+        __syncthreads();
+        // their keys that reach th (value test first; a key reaching th has a
+        // value reaching th's), every load of a thread in flight at once
+        const int nq = min(s_nq, kTopK);
+        constexpr int kPer = kCand / kSelThreads;
+        float v[kPer];
+        int idx[kPer];
 #pragma unroll
-            for (int u = 0; u < kSelUnroll; ++u) {
-                if (idx[u] >= 0 && v[u] >= thv) {
-                    const unsigned long long k = order_key(v[u], idx[u]);
-                    if (k >= th) {
-                        const int slot = atomicAdd(&s_n, 1);
-                        if (slot < kCand)
-                            s_cand[slot] = k;
-                    }
+        for (int u = 0; u < kPer; ++u) {
+            const int e = tid + u * kSelThreads;            // element e % 128 of qualifying tile e / 128
+            const int q = e / kSelTile;
+            const int i = q < nq ? s_qs[q] * kSelTile + e % kSelTile : V;
+            idx[u] = i < V ? i : -1;
+            v[u] = i < V ? lg[i] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            if (idx[u] >= 0 && v[u] >= thv) {
+                const unsigned long long k = order_key(v[u], idx[u]);
+                if (k >= th) {
+                    const int slot = atomicAdd(&s_n, 1);
+                    if (slot < kCand)
+                        s_cand[slot] = k;
                 }
             }
-        }
         __syncthreads();
         wg_top_keys<kTopK>(s_cand, min(s_n, kCand), s_top, s_wtop);
-    } else {
-        __syncthreads();
     }
 
     // outputs: wave 0, lane j of its first 16 lanes takes rank j
@@ -2525,17 +2512,23 @@ size_t workspace_need(int R, int T, int V, int H)
 }
 
 // The sampled call's workspace: past the weight-stream kernels' rows the
-// call's logits (binary32 [M, V]) follow the batch path's area.
+// call's logits (binary32 [M, V]) and the rows' best keys per vocabulary tile
+// of 128 (uint64 [M, ceil(V / 128)]) follow the batch path's area.
 size_t logits_offset(int R, int T, int V, int H)
 {
     return (workspace_need(R, T, V, H) + 255) & ~(size_t)255;
+}
+size_t item_keys_offset(int R, int T, int V, int H)
+{
+    return (logits_offset(R, T, V, H) + (size_t)R * (size_t)T * (size_t)V * sizeof(float) + 255) & ~(size_t)255;
 }
 size_t sampled_need(int R, int T, int V, int H)
 {
     const size_t base = workspace_need(R, T, V, H);
     if (base == 0 || (long long)R * T <= kStreamMaxRows)
         return base;
-    return logits_offset(R, T, V, H) + (size_t)R * (size_t)T * (size_t)V * sizeof(float);
+    return item_keys_offset(R, T, V, H) +
+           (size_t)R * (size_t)T * (size_t)((V + kRVocTile - 1) / kRVocTile) * sizeof(unsigned long long);
 }
 
 // Every argument check except the workspace's (no GPU call).
@@ -2590,10 +2583,11 @@ int record_event(void *ev, hipStream_t s, const char *what)
 int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const int32_t *draft,
                 int R, int T, int V, int H, float *lmax, int32_t *amax_ids, int32_t *nacc,
                 float *lout, const int32_t *vmap, char *wsb, int dev, hipStream_t s, void *ev0,
-                void *ev1)
+                void *ev1, unsigned long long *item_keys = nullptr)
 {
     RArgs a;
     a.vmap = vmap;
+    a.item_keys = item_keys;
     a.hidden = static_cast<const uint16_t *>(hidden);
     a.w = w;
     a.scales = static_cast<const uint16_t *>(scales);
@@ -2789,8 +2783,6 @@ int launch_sampled_rows(const void *hidden, const uint8_t *w, const void *scales
         return INT4VH_EINVAL;
     if (!aligned(ws, 256))
         return INT4VH_EALIGN;
-    if (V > kSelMaxV)
-        return INT4VH_EUNSUPPORTED;
     if (ws_bytes < sampled_need(R, T, V, H))
         return INT4VH_EWORKSPACE;
     int dev = 0;
@@ -2800,12 +2792,14 @@ int launch_sampled_rows(const void *hidden, const uint8_t *w, const void *scales
     char *wsb = static_cast<char *>(ws);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     float *lg = reinterpret_cast<float *>(wsb + logits_offset(R, T, V, H));
+    auto *tk = reinterpret_cast<unsigned long long *>(wsb + item_keys_offset(R, T, V, H));
+    const bool lse = smp.top_k == 0 || smp.lse != nullptr;
     st = launch_rows(hidden, w, scales, draft, R, T, V, H, lmax, amax_ids, nacc, lg, nullptr, wsb, dev, s, ev0,
-                     ev1);
+                     ev1, smp.top_k > 0 ? tk : nullptr);
     if (st != INT4VH_OK)
         return st;
-    const SArgs a{lg, draft, smp.topk_ids, smp.topk_logits, smp.p_draft, smp.lse, R, T, V, smp.top_k, smp.tau};
-    const bool lse = smp.top_k == 0 || smp.lse != nullptr;
+    const SArgs a{lg, tk, draft, smp.topk_ids, smp.topk_logits, smp.p_draft, smp.lse, R, T, V, smp.top_k,
+                  smp.tau};
     const dim3 grid(R * T), block(kSelThreads);
     if (smp.top_k == 0)
         hipLaunchKernelGGL((topk_rows_kernel<0, true>), grid, block, 0, s, a);

@@ -89,11 +89,13 @@ def test_sampled_workspace_bytes(lib):
     # up to 64 rows the sampled epilogue rides on the weight stream: same workspace
     for R, T in ((1, 16), (4, 16), (3, 7)):
         assert f(R, T, 151936, 5120) == g(R, T, 151936, 5120) > 0
-    # above, the call's logits follow the batch area (256-byte aligned)
-    for R, T, V in ((5, 13, 100), (64, 4, 151936), (256, 16, 8192)):
+    # above, the call's logits, then its rows' best keys per vocabulary tile
+    # of 128, follow the batch area
+    for R, T, V in ((5, 13, 100), (64, 4, 151936), (256, 16, 8192), (9, 8, 300001)):
         base = g(R, T, V, 5120)
         assert base > 0
-        assert f(R, T, V, 5120) == (base + 255) // 256 * 256 + R * T * V * 4
+        lg_end = (base + 255) // 256 * 256 + R * T * V * 4
+        assert f(R, T, V, 5120) == (lg_end + 255) // 256 * 256 + R * T * ((V + 127) // 128) * 8
     assert f(1, 0, 10, 64) == 0
     assert f(257, 16, 10, 64) == 0                    # more than 4096 rows
     assert f(1, 4, 10, 48) == 0
@@ -246,9 +248,9 @@ def test_sampled_rejects_invalid_arguments(lib):
     assert scall(tids=0) == EINVAL
     assert scall(tlog=A + 2) == EALIGN
     # more than 64 rows: the batch path, whose workspace also holds the logits
-    # and which takes vocabularies up to 262144 rows
     assert scall(R=5, T=13, ws_bytes=lib.verify_lm_head_int4_workspace_bytes(5, 13, 100, 256)) == EWORKSPACE
-    assert scall(R=5, T=13, V=262145) == EUNSUPPORTED
+    assert scall(R=5, T=13, ws_bytes=lib.verify_lm_head_int4_sampled_workspace_bytes(5, 13, 100, 256) - 1) \
+        == EWORKSPACE
     assert scall(R=257, T=16) == EINVAL               # more than 4096 rows
     assert scall(R=1, T=17) == EINVAL
     assert scall(ws_bytes=100) == EWORKSPACE

@@ -463,3 +463,26 @@ def test_batch_sampled_crowded_slice(vh, oracle_mod):
     assert np.allclose(g["p_draft"], o["p_draft"], rtol=1e-5, atol=1e-7)
     check(g, o, lg, d, qd, u, R, T, k, 1.0)
     check_own_logits(g, d, R, T, k, 1.0)
+
+
+def test_batch_sampled_full_vocab(vh, oracle_mod):
+    """More than 64 rows at the full vocabulary (V = 151936, H = 5120: 1187
+    tile keys per row): 9 requests x T = 8, top-16 at tau = 0.7 with the
+    log-sum-exp, against the oracle and on the GPU's own logits."""
+    R, T, k, tau = 9, 8, 16, 0.7
+    cfg = synth.CONFIGS["full_t16"]
+    head = synth.make_head(cfg)
+    x = np.concatenate([synth.make_hidden(cfg, s) for s in range(5)])[: R * T]
+    lg = oracle_mod.logits(x, head["packed"], head["scales"], R * T, cfg.V, cfg.H, n_threads=16)
+    inp = dict(hidden=x, packed=head["packed"], scales=head["scales"])
+    d, q, u = make_drafts(lg, R, T, k, seed=9)
+    ids, vals = sm.topk_rows(lg, k)
+    idx, mx, gap, amax = oracle_mod.argmax_rows(lg)
+    p, n = sm.sampled_accept(ids, vals, d, q, u, R, T, tau)
+    o = dict(logits=lg, logits_max=mx, argmax_ids=idx, gap=gap, amax=amax, topk_ids=ids,
+             topk_logits=vals, p_draft=p, n_accepted=n, lse=sm.lse_rows(lg, tau))
+    g = run(vh, inp, d, q, u, R, T, cfg.V, cfg.H, k, tau)
+    st = check(g, o, lg, d, q, u, R, T, k, tau)
+    st["lse_max_err"] = check_lse(g, o, lg, tau)
+    st.update(check_own_logits(g, d, R, T, k, tau))
+    say(f"full-vocab 9 x T=8 (batch path) stats {st}")
