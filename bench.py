@@ -97,24 +97,28 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_106_081, write=73_920, source="int4vh.hip",
-                      source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "full_t8": dict(read=390_428_077, write=41_088, source="int4vh.hip",
-                     source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "two_blocks_t16": dict(read=393_092_283, write=74_048, source="int4vh.hip",
-                            source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "batch": dict(read=684_007_154, write=1_062_176, source="int4vh.hip",
-                   source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "draft_vocab": dict(read=21_341_596, write=17_536, source="int4vh.hip",
-                         source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "shard_t16": dict(read=50_769_449, write=74_944, source="int4vh.hip",
-                       source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "full_t16_top16": dict(read=391_756_697, write=568_576, source="int4vh.hip",
-                            source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "full_t16_top0": dict(read=391_539_208, write=358_912, source="int4vh.hip",
-                           source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
-    "two_blocks_t16_top16": dict(read=393_708_850, write=570_816, source="int4vh.hip",
-                                  source_sha256="40ae4357caeaa3dbf18f2b3464ee7ecaad8307cc5981f0daf902838d9bed63f7"),
+    "full_t16": dict(read=391_098_914, write=73_920, source="int4vh.hip",
+                     source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "full_t8": dict(read=390_432_177, write=41_088, source="int4vh.hip",
+                    source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "two_blocks_t16": dict(read=393_095_866, write=74_048, source="int4vh.hip",
+                           source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "batch": dict(read=684_018_609, write=1_062_176, source="int4vh.hip",
+                  source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "draft_vocab": dict(read=21_348_111, write=17_536, source="int4vh.hip",
+                        source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "shard_t16": dict(read=50_762_281, write=74_944, source="int4vh.hip",
+                      source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "full_t16_top16": dict(read=391_754_980, write=568_576, source="int4vh.hip",
+                           source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "full_t16_top0": dict(read=391_537_893, write=358_912, source="int4vh.hip",
+                          source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "two_blocks_t16_top16": dict(read=393_707_927, write=570_816, source="int4vh.hip",
+                                 source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "batch_top16": dict(read=684_106_957, write=159_544_909, source="int4vh.hip",
+                        source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "batch_top0": dict(read=684_094_804, write=156_644_640, source="int4vh.hip",
+                       source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
