@@ -432,11 +432,11 @@ def test_sampled_then_greedy_workspace_reuse(vh, R, T):
 
 def test_batch_sampled_crowded_slice(vh, oracle_mod):
     """More than 64 rows, integer-exact logits built so that each row's
-    largest values all sit in one thread's slice of the row selection (rows
-    v = c0, c0 + 512, ...) and tie with each other and with a crowd of
-    second-largest values: the candidates come from few slices and the order
-    falls to the lowest rows.  Top-k ids and logits equal the oracle's bit
-    for bit, and p(d) the oracle's formula on them."""
+    largest values tie at rows v = c0, c0 + 512, ... (one row in every fourth
+    vocabulary tile of 128) above a crowd of tied second-largest values (every
+    third row): the selection's threshold and candidates rest on tied keys and
+    the order falls to the lowest rows.  Top-k ids and logits equal the
+    oracle's bit for bit, and p(d) the oracle's formula on them."""
     R, T, V, H, k = 33, 2, 10000, 64, 16
     M = R * T
     say(f"crowded slice R={R} T={T} V={V} H={H} k={k}")
