@@ -222,7 +222,7 @@ def check(g, o, lg, d, q, u, R, T, k, tau):
                                            (9, 8, 5000, 512, 16, 1.0), (33, 4, 4097, 256, 8, 0.7),
                                            (65, 1, 2000, 96, 5, 2.0), (16, 16, 3000, 128, 16, 0.3),
                                            (100, 3, 600, 64, 12, 1.3), (8, 10, 300, 64, 16, 1.0),
-                                           (13, 5, 12, 64, 12, 1.0)])
+                                           (13, 5, 12, 64, 12, 1.0), (13, 5, 300001, 64, 16, 1.0)])
 def test_sampled_parity(vh, oracle_mod, R, T, V, H, k, tau):
     say(f"sampled R={R} T={T} V={V} H={H} k={k} tau={tau}")
     inp = synth.uniform_inputs(R * T, V, H, seed=R * 31 + T + V + H + k)
@@ -486,3 +486,25 @@ def test_batch_sampled_full_vocab(vh, oracle_mod):
     st["lse_max_err"] = check_lse(g, o, lg, tau)
     st.update(check_own_logits(g, d, R, T, k, tau))
     say(f"full-vocab 9 x T=8 (batch path) stats {st}")
+
+
+@pytest.mark.parametrize("R,T,k", [(9, 8, 16), (33, 2, 8)])
+def test_batch_sampled_without_lse(vh, R, T, k):
+    """More than 64 rows without the log-sum-exp (the selection's top-k-only
+    instance): top-k ids and logits, p(d) and the accepted counts equal the
+    call that also returns the log-sum-exp, bit for bit."""
+    V, H = 7000, 256
+    inp = synth.uniform_inputs(R * T, V, H, seed=R + T + k)
+    x = dev(inp["hidden"], torch.float16).reshape(R, T, H)
+    w = dev(inp["packed"])
+    s = dev(inp["scales"], torch.float16)
+    rng = np.random.default_rng(k)
+    d = dev(rng.integers(0, V, (R, T - 1), dtype=np.int32))
+    q = dev(rng.uniform(0.3, 1.0, (R, T - 1)).astype(np.float32))
+    u = dev(rng.random((R, T - 1)).astype(np.float32))
+    a1 = vh.verify_sampled(x, w, s, d, q, u, top_k=k, temperature=0.8)
+    a2 = vh.verify_sampled(x, w, s, d, q, u, top_k=k, temperature=0.8, want_lse=True)
+    torch.cuda.synchronize()
+    assert a1[6] is None and a2[6] is not None
+    for t1, t2 in zip(a1[:6], a2[:6]):
+        assert torch.equal(t1, t2)
