@@ -1068,6 +1068,13 @@ verify_kernel(Args a)
     // token) so the loads are straight-line and all in flight together.
     constexpr int kRowsPerTok = (16 + kP - 1) / kP < 3 ? (16 + kP - 1) / kP : 3;
     const int rt = rlane ? rtok : 0;
+    // In token groups the lanes of a partial group's missing rows take the
+    // epilogue's steps as well (on token 0's sums and the step exponent
+    // staged for an empty row; nothing of theirs is published).  Every
+    // group's workgroups then spend the same time per tile and stay in step:
+    // a partial group that runs ahead drifts out of the window of tiles the
+    // XCD's L2 still holds, and the full groups fetch those tiles again.
+    const bool rwork = lane < 32 && (rtok < Mg || n_g > 1);
     auto reduce_tile = [&](int k) {
         const int buf = k & 1;
         double code = 0.0;                 // integer-valued, |code| < 2^47: exact
@@ -1077,7 +1084,7 @@ verify_kernel(Args a)
             for (int w = 0; w < kWaves; ++w)
                 code += __longlong_as_double((long long)s_part[buf][w][rt + kP * j][n16]);
         unsigned long long key = 0ull;
-        if (rlane) {
+        if (rwork) {
             const int v = (tset + k * n_sets) * kTileRows + n16;
             const float val = (float)ldexp(code, rexp);   // the one rounding
             if (v < V) {
@@ -1096,7 +1103,7 @@ verify_kernel(Args a)
                         __hip_atomic_store(&a.draft_seen[grow], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
-                if (kLogits)
+                if (kLogits && rlane)
                     a.logits_out[(size_t)(kMaxRows * tgrp + rtok) * V + v] = val;
             }
         }
