@@ -97,28 +97,28 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_098_914, write=73_920, source="int4vh.hip",
-                     source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "full_t8": dict(read=390_432_177, write=41_088, source="int4vh.hip",
-                    source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "two_blocks_t16": dict(read=393_095_866, write=74_048, source="int4vh.hip",
-                           source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "batch": dict(read=684_018_609, write=1_062_176, source="int4vh.hip",
-                  source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "draft_vocab": dict(read=21_348_111, write=17_536, source="int4vh.hip",
-                        source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "shard_t16": dict(read=50_762_281, write=74_944, source="int4vh.hip",
-                      source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "full_t16_top16": dict(read=391_754_980, write=568_576, source="int4vh.hip",
-                           source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "full_t16_top0": dict(read=391_537_893, write=358_912, source="int4vh.hip",
-                          source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "two_blocks_t16_top16": dict(read=393_707_927, write=570_816, source="int4vh.hip",
-                                 source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "batch_top16": dict(read=684_106_957, write=159_544_909, source="int4vh.hip",
-                        source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
-    "batch_top0": dict(read=684_094_804, write=156_644_640, source="int4vh.hip",
-                       source_sha256="f21127c32b658dc001f65d87582525db0f3721419e30bdcbb0fe453d2bade05e"),
+    "full_t16": dict(read=391_075_193, write=73_920, source="int4vh.hip",
+                     source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "full_t8": dict(read=390_385_235, write=41_088, source="int4vh.hip",
+                    source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "two_blocks_t16": dict(read=393_060_194, write=74_048, source="int4vh.hip",
+                           source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "batch": dict(read=683_933_418, write=1_062_176, source="int4vh.hip",
+                  source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "draft_vocab": dict(read=21_351_003, write=17_536, source="int4vh.hip",
+                        source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "shard_t16": dict(read=50_771_309, write=74_944, source="int4vh.hip",
+                      source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "full_t16_top16": dict(read=391_709_262, write=568_576, source="int4vh.hip",
+                           source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "full_t16_top0": dict(read=391_496_194, write=358_912, source="int4vh.hip",
+                          source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "two_blocks_t16_top16": dict(read=393_664_427, write=570_816, source="int4vh.hip",
+                                 source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "batch_top16": dict(read=684_049_022, write=159_546_336, source="int4vh.hip",
+                        source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
+    "batch_top0": dict(read=684_044_823, write=156_644_640, source="int4vh.hip",
+                       source_sha256="8ef45de0503ed866c1312d88f37cab06bead407b59816cce8f52a330a7602f37"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="98095b9a5be96d9d8f9234b39037c2cd2d9c5ff5914a87e75fa070500f7786bf"),
 }
@@ -340,16 +340,17 @@ def bench_stream(args):
     print(json.dumps(result), flush=True)
 
 
-SWEEP_ROWS = (1, 2, 4, 8, 16, 17, 24, 32, 48, 64, 96, 128, 192, 256, 512)
+SWEEP_ROWS = (1, 2, 4, 8, 16, 17, 20, 24, 28, 32, 40, 48, 56, 64, 96, 128, 192, 256, 512)
 
 
 def bench_sweep(args):
     """Cost of one verify call against the number of rows M it verifies (M
-    requests of one position each: the weight-stream path up to 16 rows, the
-    matrix-core path beyond), full-vocabulary head V=151936, H=5120, two head
-    copies rotated.  Per M: the whole call in a HIP graph of 20 calls
+    requests of one position each: the weight-stream path up to 16 rows,
+    token groups of 16 up to 64, the matrix-core batch path beyond),
+    full-vocabulary head V=151936, H=5120, two head copies rotated.  Per M: the whole call in a HIP graph of 20 calls
     (replayed after an untimed warm-up) and the main kernel alone (HIP events,
-    eager).  The leg's value is the verified rows/s at M = 32."""
+    eager).  The leg's value is the verified rows/s at M = 32 (with
+    --sweep-rows not naming 32: at the largest M named)."""
     import torch
     from int4_output_head_amd import binding, synth
 
@@ -360,12 +361,17 @@ def bench_sweep(args):
     w0 = torch.from_numpy(head["packed"]).to(dev)
     ws = [w0, w0.clone()]
     s = torch.from_numpy(head["scales"]).view(torch.float16).to(dev)
-    rows_max = max(SWEEP_ROWS)
+    rows = tuple(int(m) for m in args.sweep_rows.split(",")) if args.sweep_rows else SWEEP_ROWS
+    if not rows or min(rows) < 1 or max(rows) > 4096:
+        raise SystemExit("--sweep-rows: row counts from 1 to 4096")
+    rows_max = max(rows)
     rng = np.random.default_rng(0)
     x_all = torch.from_numpy(synth.f16_bits(rng.standard_normal((rows_max, cfg.H)))).view(torch.float16).to(dev)
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy:
+        calibration_copy(torch, dev)
     curve = []
-    for M in SWEEP_ROWS:
+    for M in rows:
         x = x_all[:M].reshape(M, 1, cfg.H).contiguous()
         work = binding.Workspace(binding.workspace_bytes(M, 1, cfg.V, cfg.H), dev)
         for i in range(10):
@@ -407,15 +413,18 @@ def bench_sweep(args):
         log(f"sweep {rec}")
         del work, g
     at = {r["M"]: r for r in curve}
+    m_val = 32 if 32 in at else max(at)
     result = {
         "metric": "int4 lm_head verify: verified rows/s against rows per call (full vocabulary)",
-        "value": at[32]["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": 100, "warmup": 10,
-        "ms_per_step": round(at[32]["us_per_call"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
+        "value": at[m_val]["rows_per_s"], "unit": "rows/s", "n_gpus": 1, "steps": 100, "warmup": 10,
+        "ms_per_step": round(at[m_val]["us_per_call"] / 1e3, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": DTYPE, "data": "synthetic",
-        "config": {"workload": "verify calls of M rows, V=151936 H=5120, M in " + str(list(SWEEP_ROWS)),
+        "config": {"workload": "verify calls of M rows, V=151936 H=5120, M in " + str(list(rows)),
+                   "value_at_rows": m_val,
                    "timing": "HIP graph of 20 calls replayed 5x per M; main kernel by HIP events"},
         "curve": curve,
-        "ratio_32_to_16_rows": round(at[32]["us_per_call"] / at[16]["us_per_call"], 3),
+        "ratio_32_to_16_rows": (round(at[32]["us_per_call"] / at[16]["us_per_call"], 3)
+                                if 32 in at and 16 in at else None),
         "cpu_baseline": None,
         "cpu_baseline_note": "the oracle's cost grows linearly with M; see the full_t16 and batch legs",
     }
@@ -511,6 +520,8 @@ def main():
     ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--full-softmax", action="store_true",
                     help="sampled verification over the whole vocabulary (top_k = 0)")
+    ap.add_argument("--sweep-rows", default="",
+                    help="--config sweep: comma-separated row counts (default: the whole curve)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain device copy of head-sized buffers (a known "
                          "number of bytes) to scale hardware byte counters")
