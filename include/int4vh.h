@@ -144,11 +144,12 @@ int verify_lm_head_int4_batch(const void *hidden, const uint8_t *packed_w, const
                               void *stream);
 
 /* The batch call, instrumented: event_before and event_after (hipEvent_t
- * handles owned by the caller, created on the stream's device; NULL skips a
- * record) are recorded on `stream` immediately before and after the main
- * verify kernel, after the staging kernel, so that hipEventElapsedTime gives
- * the main kernel's duration alone.  Same arguments, results and errors as
- * verify_lm_head_int4_batch; a failed record returns INT4VH_EHIP.  For
+ * handles owned by the caller, created on the stream's device; either may be
+ * NULL) take the start and end timestamps of the main verify kernel's own
+ * dispatch (the staging kernel runs before it, untimed), so that
+ * hipEventElapsedTime gives the main kernel's duration alone, as a kernel
+ * trace measures it.  Same arguments, results and errors as
+ * verify_lm_head_int4_batch; a failed launch returns INT4VH_EHIP.  For
  * measuring the weight stream (or the matrix cores) against its roofline. */
 int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
                                     const void *scales, const int32_t *draft_ids, int R, int T,
@@ -246,8 +247,10 @@ int verify_lm_head_int4_sampled(const void *hidden, const uint8_t *packed_w, con
                                 void *stream);
 
 /* The sampled call, instrumented like verify_lm_head_int4_batch_timed:
- * event_before / event_after (caller-owned hipEvent_t, NULL to skip) are
- * recorded on `stream` right around the main verify kernel. */
+ * event_before / event_after (caller-owned hipEvent_t, either may be NULL)
+ * take the start and end timestamps of the main verify kernel's dispatch
+ * (the batch kernel above 64 rows; the selection and acceptance kernels
+ * after it are untimed). */
 int verify_lm_head_int4_sampled_timed(const void *hidden, const uint8_t *packed_w,
                                       const void *scales, const int32_t *draft_ids,
                                       const float *draft_probs, const float *uniforms, int R, int T,

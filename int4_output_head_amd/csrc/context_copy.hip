@@ -23,6 +23,7 @@
 namespace {
 
 using int4vh_detail::hip_fail;
+using int4vh_detail::launch_timed;
 
 constexpr int kThreads = 1024;
 constexpr int kMaxKey = 64;
@@ -101,14 +102,6 @@ bool aligned(const void *p, size_t al)
     return ((uintptr_t)p % al) == 0;
 }
 
-int record_event(void *ev, hipStream_t s, const char *what)
-{
-    if (!ev)
-        return INT4VH_OK;
-    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev), s);
-    return e == hipSuccess ? INT4VH_OK : hip_fail(e, what);
-}
-
 } // namespace
 
 extern "C" {
@@ -130,15 +123,11 @@ int context_copy_propose_timed(const int32_t *prompts, const int64_t *prompt_off
         !aligned(out_match_len, 4))
         return INT4VH_EALIGN;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    int st = record_event(event_before, s, "event record before context-copy kernel");
-    if (st != INT4VH_OK)
-        return st;
-    hipLaunchKernelGGL(context_copy_kernel, dim3(R), dim3(kThreads), 0, s, prompts, prompt_offsets, keys,
-                       n_max, n_min, n_out, out_tokens, out_count, out_match_end, out_match_len);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return hip_fail(e, "context-copy kernel launch");
-    return record_event(event_after, s, "event record after context-copy kernel");
+    // the events take the kernel's own start and end (launch_timed)
+    const hipError_t e = launch_timed(context_copy_kernel, dim3(R), dim3(kThreads), s, event_before, event_after,
+                                      prompts, prompt_offsets, keys, n_max, n_min, n_out, out_tokens, out_count,
+                                      out_match_end, out_match_len);
+    return e == hipSuccess ? INT4VH_OK : hip_fail(e, "context-copy kernel launch");
 }
 
 int context_copy_propose(const int32_t *prompts, const int64_t *prompt_offsets, int R,

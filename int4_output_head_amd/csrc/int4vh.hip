@@ -2341,6 +2341,7 @@ int hip_fail(hipError_t e, const char *what)
 }
 
 using int4vh_detail::cu_count;
+using int4vh_detail::launch_timed;
 
 bool aligned(const void *p, size_t al)
 {
@@ -2578,12 +2579,12 @@ int validate(const void *hidden, const uint8_t *w, const void *scales, const int
     return INT4VH_OK;
 }
 
-// Records ev (a hipEvent_t, may be null) on stream s.
-int record_event(void *ev, hipStream_t s, const char *what)
+// The main kernel of a call, timed by ev0 / ev1 when given (launch_timed).
+template <typename A>
+int launch_main(void (*kernel)(A), dim3 grid, dim3 block, hipStream_t s, void *ev0, void *ev1, const A &a,
+                const char *what)
 {
-    if (!ev)
-        return INT4VH_OK;
-    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev), s);
+    const hipError_t e = launch_timed(kernel, grid, block, s, ev0, ev1, a);
     return e == hipSuccess ? INT4VH_OK : hip_fail(e, what);
 }
 
@@ -2630,17 +2631,8 @@ int launch_rows(const void *hidden, const uint8_t *w, const void *scales, const 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return hip_fail(e, "stage_rows kernel launch");
-    int st = record_event(ev0, s, "event record before verify_rows kernel");
-    if (st != INT4VH_OK)
-        return st;
-    if (lout)
-        hipLaunchKernelGGL(verify_rows_kernel<true>, dim3(grid), dim3(kRThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL(verify_rows_kernel<false>, dim3(grid), dim3(kRThreads), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return hip_fail(e, "verify_rows kernel launch");
-    return record_event(ev1, s, "event record after verify_rows kernel");
+    return launch_main(lout ? verify_rows_kernel<true> : verify_rows_kernel<false>, dim3(grid), dim3(kRThreads), s,
+                       ev0, ev1, a, "verify_rows kernel launch");
 }
 
 // Outputs and parameters of the sampled epilogue.
@@ -2766,14 +2758,7 @@ int launch_verify(const void *hidden, const uint8_t *w, const void *scales, cons
         if (e != hipSuccess)
             return hip_fail(e, "stage kernel launch");
     }
-    const int rs = record_event(ev0, s, "event record before verify kernel");
-    if (rs != INT4VH_OK)
-        return rs;
-    hipLaunchKernelGGL(fn.verify, dim3(grid), dim3(kThreads), 0, s, a);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return hip_fail(e, "verify kernel launch");
-    return record_event(ev1, s, "event record after verify kernel");
+    return launch_main(fn.verify, dim3(grid), dim3(kThreads), s, ev0, ev1, a, "verify kernel launch");
 }
 
 // Sampled call of more than 64 rows: the batch kernels with the logits

@@ -53,6 +53,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 using int4vh_detail::cu_count;
+using int4vh_detail::launch_timed;
 using int4vh_detail::hip_fail;
 
 constexpr int kAmaxThreads = 256;               // 4 waves
@@ -245,14 +246,6 @@ int launched(const char *what)
     return e == hipSuccess ? INT4VH_OK : hip_fail(e, what);
 }
 
-int record_event(void *ev, hipStream_t s, const char *what)
-{
-    if (!ev)
-        return INT4VH_OK;
-    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev), s);
-    return e == hipSuccess ? INT4VH_OK : hip_fail(e, what);
-}
-
 int do_amax(const void *acts, int dtype, int N, int H, float *amax, int accumulate, void *stream)
 {
     if (!acts || !amax || N < 1 || !h_ok(H) || !dtype_ok(dtype))
@@ -321,22 +314,13 @@ int do_pack(const void *W, int dtype, int V, int H, const void *scales, uint8_t 
     const long long waves = n_chunks < stride ? n_chunks : stride;
     const unsigned blocks = (unsigned)((waves + 3) / 4);
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    int st = record_event(ev0, s, "event record before pack kernel");
-    if (st != INT4VH_OK)
-        return st;
     const uint16_t *w = static_cast<const uint16_t *>(W);
     const uint16_t *sc = static_cast<const uint16_t *>(scales);
     uint32_t *out = reinterpret_cast<uint32_t *>(packed);
-    if (dtype == INT4VH_F16)
-        hipLaunchKernelGGL(pack_kernel<INT4VH_F16>, dim3(blocks), dim3(kPackThreads), 0, s, w, sc, H,
-                           n_elems, n_chunks, stride, out);
-    else
-        hipLaunchKernelGGL(pack_kernel<INT4VH_BF16>, dim3(blocks), dim3(kPackThreads), 0, s, w, sc, H,
-                           n_elems, n_chunks, stride, out);
-    st = launched("pack kernel launch");
-    if (st != INT4VH_OK)
-        return st;
-    return record_event(ev1, s, "event record after pack kernel");
+    // ev0 / ev1 take the pack kernel's own start and end (launch_timed)
+    e = launch_timed(dtype == INT4VH_F16 ? pack_kernel<INT4VH_F16> : pack_kernel<INT4VH_BF16>, dim3(blocks),
+                     dim3(kPackThreads), s, ev0, ev1, w, sc, H, n_elems, n_chunks, stride, out);
+    return e == hipSuccess ? INT4VH_OK : hip_fail(e, "pack kernel launch");
 }
 
 } // namespace

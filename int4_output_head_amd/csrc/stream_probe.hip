@@ -103,25 +103,15 @@ int int4vh_stream_read(const void *buf, size_t bytes, int mode, uint32_t *out, v
         grid = INT4VH_PROBE_OUT_WORDS / kWaves;
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const size_t n_blocks = bytes / 1024;
-    if (event_before) {
-        e = hipEventRecord(static_cast<hipEvent_t>(event_before), s);
-        if (e != hipSuccess)
-            return int4vh_detail::hip_fail(e, "event record before stream kernel");
-    }
+    // the events take the kernel's own start and end (launch_timed)
     if (mode == 0)
-        hipLaunchKernelGGL(stream_regs_kernel, dim3(grid), dim3(kThreads), 0, s,
-                           static_cast<const u32x4 *>(buf), n_blocks, out);
+        e = int4vh_detail::launch_timed(stream_regs_kernel, dim3(grid), dim3(kThreads), s, event_before,
+                                        event_after, static_cast<const u32x4 *>(buf), n_blocks, out);
     else
-        hipLaunchKernelGGL(stream_lds_kernel, dim3(grid), dim3(kThreads), 0, s,
-                           static_cast<const uint8_t *>(buf), n_blocks, out);
-    e = hipGetLastError();
+        e = int4vh_detail::launch_timed(stream_lds_kernel, dim3(grid), dim3(kThreads), s, event_before,
+                                        event_after, static_cast<const uint8_t *>(buf), n_blocks, out);
     if (e != hipSuccess)
         return int4vh_detail::hip_fail(e, "stream kernel launch");
-    if (event_after) {
-        e = hipEventRecord(static_cast<hipEvent_t>(event_after), s);
-        if (e != hipSuccess)
-            return int4vh_detail::hip_fail(e, "event record after stream kernel");
-    }
     return 0;
 }
 
