@@ -150,7 +150,10 @@ int verify_lm_head_int4_batch(const void *hidden, const uint8_t *packed_w, const
  * hipEventElapsedTime gives the main kernel's duration alone, as a kernel
  * trace measures it.  Same arguments, results and errors as
  * verify_lm_head_int4_batch; a failed launch returns INT4VH_EHIP.  For
- * measuring the weight stream (or the matrix cores) against its roofline. */
+ * measuring the weight stream (or the matrix cores) against its roofline;
+ * under HIP graph capture call it with both events NULL (or call
+ * verify_lm_head_int4_batch), since events attached to a dispatch are not
+ * part of the capturable API. */
 int verify_lm_head_int4_batch_timed(const void *hidden, const uint8_t *packed_w,
                                     const void *scales, const int32_t *draft_ids, int R, int T,
                                     int V, int H, float *logits_max, int32_t *argmax_ids,

@@ -48,8 +48,9 @@ int context_copy_propose(const int32_t *prompts, const int64_t *prompt_offsets, 
                          void *stream);
 
 /* The call instrumented for measurement: event_before / event_after
- * (caller-owned hipEvent_t, NULL to skip) recorded on `stream` right around
- * the kernel. */
+ * (caller-owned hipEvent_t, either may be NULL) take the start and end
+ * timestamps of the kernel's own dispatch; not for use under HIP graph
+ * capture. */
 int context_copy_propose_timed(const int32_t *prompts, const int64_t *prompt_offsets, int R,
                                const int32_t *keys, int n_max, int n_min, int n_out,
                                int32_t *out_tokens, int32_t *out_count, int32_t *out_match_end,

@@ -32,8 +32,8 @@ extern "C" {
  * [INT4VH_PROBE_OUT_WORDS], caller-owned) receives one word per wave: in mode
  * 0 the xor of every 32-bit word the wave read (so the xor of all of `out`
  * is the xor of the whole buffer), in mode 1 zero.  event_before /
- * event_after (hipEvent_t, NULL to skip) are recorded right around the
- * kernel.  Returns 0, INT4VH_PROBE_EINVAL (NULL pointer, bytes 0 or not a
+ * event_after (hipEvent_t, either may be NULL) take the start and end
+ * timestamps of the kernel's own dispatch.  Returns 0, INT4VH_PROBE_EINVAL (NULL pointer, bytes 0 or not a
  * multiple of 1024, buf not 16-byte aligned, out not 4-byte aligned, mode not
  * 0 or 1), or INT4VH_EHIP (-4) with the text in
  * verify_lm_head_int4_last_error(). */

@@ -84,8 +84,9 @@ int requant_lm_head_int4(const void *W, int w_dtype, int V, int H, const void *a
                          void *stream);
 
 /* The pack step, instrumented for measurement: event_before and event_after
- * (caller-owned hipEvent_t handles, NULL to skip) are recorded on `stream`
- * immediately around the quantise-and-pack kernel. */
+ * (caller-owned hipEvent_t handles, either may be NULL) take the start and
+ * end timestamps of the quantise-and-pack kernel's own dispatch
+ * (hipExtLaunchKernel); not for use under HIP graph capture. */
 int requant_lm_head_int4_pack_timed(const void *W, int dtype, int V, int H, const void *scales,
                                     uint8_t *packed, void *stream, void *event_before,
                                     void *event_after);

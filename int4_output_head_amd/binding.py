@@ -165,9 +165,10 @@ def verify_batch(hidden, packed_w, scales, draft_ids=None, *, R: int | None = No
     R given); packed_w: uint8 [V, H/2]; scales: float16 [H]; draft_ids: int32
     [R, T-1] (None when T == 1).  Returns (logits_max [R*T], argmax_ids [R*T],
     n_accepted [R]) and, with logits=True, logits [R*T, V] as a 4th item.
-    events=(before, after), two torch.cuda.Event(enable_timing=True), are
-    recorded on the current stream right around the main verify kernel (the
-    instrumented entry point verify_lm_head_int4_batch_timed)."""
+    events=(before, after), two torch.cuda.Event(enable_timing=True), take
+    the start and end timestamps of the main verify kernel's own dispatch
+    (the instrumented entry point verify_lm_head_int4_batch_timed; not for
+    use under graph capture)."""
     if hidden.dim() == 3:
         R, T, H = hidden.shape
         hidden = hidden.reshape(R * T, H)
@@ -332,8 +333,8 @@ def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, u
     topk_logits [R*T, k], p_draft [R, T-1], n_accepted [R], lse [R*T]) (the
     top-k outputs are None when top_k == 0; lse, the log-sum-exp of
     logit / temperature over the vocabulary, is None unless want_lse or
-    top_k == 0).  events=(before, after) are recorded right around the main
-    verify kernel.  Above 64 rows the workspace also holds the call's logits
+    top_k == 0).  events=(before, after) take the start and end timestamps of
+    the main verify kernel's dispatch.  Above 64 rows the workspace also holds the call's logits
     (sampled_workspace_bytes)."""
     if hidden.dim() == 3:
         R, T, H = hidden.shape
@@ -501,7 +502,8 @@ def requant_scales(amax) -> torch.Tensor:
 def requant_pack(W, scales, *, events=None) -> torch.Tensor:
     """Quantise the head W [V, H] (float16 or bfloat16) with per-channel
     scales (float16 [H]) and pack it: uint8 [V, H/2] in the verify layout.
-    events=(before, after) are recorded right around the pack kernel."""
+    events=(before, after) take the start and end timestamps of the pack
+    kernel's dispatch."""
     if not isinstance(W, torch.Tensor) or not W.is_cuda:
         raise TypeError("W must be a CUDA (HIP) tensor")
     dt = _dtype_code(W, "W")
@@ -557,7 +559,7 @@ def context_copy(prompts, offsets, keys, *, n_min: int = 1, n_out: int = 8, even
     [total] (all prompts back to back); offsets: int64 [R+1]; keys: int32
     [R, n_max] (the last n_max tokens of each sequence).  Returns (tokens
     int32 [R, n_out] (-1 past count), count [R], match_end [R], match_len
-    [R])."""
+    [R]).  events=(before, after) take the kernel's dispatch start and end."""
     _check(prompts, "prompts", torch.int32, 1)
     _check(offsets, "offsets", torch.int64, 1)
     _check(keys, "keys", torch.int32, 2)
@@ -590,7 +592,8 @@ def stream_read(buf, mode: int = 0, *, out=None, events=None):
     """Read the device tensor `buf` once (int4vh_stream_read): mode 0 loads
     into registers, mode 1 copies into LDS like the verify kernel.  Returns
     the per-wave words (uint32 as int32 [8192]); in mode 0 their xor is the
-    xor of the buffer's 32-bit words."""
+    xor of the buffer's 32-bit words.  events=(before, after) take the
+    kernel's dispatch start and end."""
     if not isinstance(buf, torch.Tensor) or not buf.is_cuda or not buf.is_contiguous():
         raise TypeError("buf must be a contiguous CUDA (HIP) tensor")
     dev = buf.device
