@@ -367,9 +367,7 @@ def bench_sweep(args):
     w0 = torch.from_numpy(head["packed"]).to(dev)
     ws = [w0, w0.clone()]
     s = torch.from_numpy(head["scales"]).view(torch.float16).to(dev)
-    rows = tuple(int(m) for m in args.sweep_rows.split(",")) if args.sweep_rows else SWEEP_ROWS
-    if not rows or min(rows) < 1 or max(rows) > 4096:
-        raise SystemExit("--sweep-rows: row counts from 1 to 4096")
+    rows = args.sweep_rows or SWEEP_ROWS
     rows_max = max(rows)
     rng = np.random.default_rng(0)
     x_all = torch.from_numpy(synth.f16_bits(rng.standard_normal((rows_max, cfg.H)))).view(torch.float16).to(dev)
@@ -542,6 +540,14 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path runs on a single MI355X; see the sharding notes)", file=sys.stderr)
         sys.exit(2)
+    if args.sweep_rows:
+        try:
+            args.sweep_rows = tuple(int(m) for m in args.sweep_rows.split(","))
+        except ValueError:
+            args.sweep_rows = ()
+        if not args.sweep_rows or min(args.sweep_rows) < 1 or max(args.sweep_rows) > 4096:
+            print("--sweep-rows: comma-separated row counts from 1 to 4096", file=sys.stderr)
+            sys.exit(2)
 
     if args.config == "requant":
         bench_requant(args)

@@ -153,7 +153,10 @@ def _check(t, name, dtype, ndim=None):
 
 
 def _event_handle(ev, stream):
-    """Raw hipEvent_t of a torch.cuda.Event (created by a first record)."""
+    """Raw hipEvent_t of a torch.cuda.Event (created by a first record);
+    None gives a null handle (that end of the kernel is not timed)."""
+    if ev is None:
+        return ctypes.c_void_p(None)
     if ev.cuda_event == 0:
         ev.record(stream)
     return ctypes.c_void_p(ev.cuda_event)
@@ -334,8 +337,8 @@ def verify_sampled(hidden, packed_w, scales, draft_ids=None, draft_probs=None, u
     top-k outputs are None when top_k == 0; lse, the log-sum-exp of
     logit / temperature over the vocabulary, is None unless want_lse or
     top_k == 0).  events=(before, after) take the start and end timestamps of
-    the main verify kernel's dispatch.  Above 64 rows the workspace also holds the call's logits
-    (sampled_workspace_bytes)."""
+    the main verify kernel's dispatch.  Above 64 rows the workspace also
+    holds the call's logits (sampled_workspace_bytes)."""
     if hidden.dim() == 3:
         R, T, H = hidden.shape
         hidden = hidden.reshape(R * T, H)

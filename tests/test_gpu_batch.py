@@ -307,3 +307,9 @@ def test_timed_entry_point(vh, orc, R, T):
     t_kernel = e[1].elapsed_time(e[2])
     t_call = e[0].elapsed_time(e[3])
     assert 0 < t_kernel <= t_call
+    # either event alone (the other end untimed) is accepted and changes nothing
+    for evs in ((e[1], None), (None, e[2])):
+        one = vh.verify_batch(x, w, s, dr, logits=True, workspace=ws, events=evs)
+        torch.cuda.synchronize()
+        for a, b in zip(plain, one):
+            assert torch.equal(a, b)
