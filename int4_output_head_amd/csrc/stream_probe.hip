@@ -1,6 +1,6 @@
 // stream_probe.hip -- read-only HBM streaming kernels: the reference line for
 // "how fast can this GPU read a head-sized buffer once", against which the
-// verify kernel's weight stream is judged.  Two load paths:
+// verify kernel's weight stream is compared.  Two load paths:
 //
 //   mode 0  every lane loads 16 bytes per instruction into registers
 //           (global_load_dwordx4, non-temporal), 8 loads in flight per lane,
