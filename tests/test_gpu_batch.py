@@ -70,10 +70,11 @@ def drafts_from(ids, R, T, V, rng):
 
 
 # (R, T, V, H): token groups of 16 (17-64 rows) with a partial last group of
-# 1, 8 and 7 rows, one 128-row tile, partial tiles, several tiles, a ragged
+# 1, 8, 7 and 5 rows (the last with a ragged 16-row tile and H below one
+# 128-channel unit), one 128-row tile, partial tiles, several tiles, a ragged
 # last tile, H below one 128-channel step and not a multiple of it, V not a
 # multiple of the 128-row vocabulary tile, the 4096-row maximum
-CASES = [(17, 1, 1000, 256), (3, 8, 1000, 256), (5, 11, 2500, 640), (4, 8, 3000, 512),
+CASES = [(17, 1, 1000, 256), (3, 8, 1000, 256), (5, 11, 2500, 640), (3, 7, 129, 32), (4, 8, 3000, 512),
          (64, 2, 2000, 1024), (33, 4, 4097, 640), (64, 4, 1500, 5120), (130, 3, 700, 96),
          (40, 5, 129, 32), (9, 16, 5003, 2080), (256, 16, 300, 128), (4096, 1, 257, 64)]
 
