@@ -216,7 +216,8 @@ def check(g, o, lg, d, q, u, R, T, k, tau):
                                            # more than 16 rows: token groups of 16
                                            (2, 16, 5000, 512, 16, 1.0), (3, 11, 4097, 256, 8, 0.7),
                                            (4, 16, 3000, 128, 16, 1.3), (17, 1, 2000, 96, 5, 2.0),
-                                           (5, 12, 20000, 1024, 16, 0.3),
+                                           (5, 12, 20000, 1024, 16, 0.3), (3, 8, 4097, 256, 16, 1.0),
+                                           (7, 8, 3000, 128, 8, 0.7),
                                            # more than 64 rows: the batch kernels' logits and
                                            # the per-row selection
                                            (9, 8, 5000, 512, 16, 1.0), (33, 4, 4097, 256, 8, 0.7),
@@ -272,7 +273,8 @@ def check_full_softmax(g, o, lg, d, q, u, R, T, tau):
                                          (4, 4, 999, 96, 2.0), (1, 8, 151936, 5120, 1.0),
                                          (1, 16, 20000, 1024, 0.7), (2, 4, 3000, 256, 1.3),
                                          (2, 16, 5000, 512, 1.0), (4, 16, 3000, 256, 0.7),
-                                         (3, 7, 4097, 96, 2.0),
+                                         (3, 7, 4097, 96, 2.0), (5, 8, 3000, 256, 1.3),
+                                         (13, 3, 2000, 96, 0.7),
                                          # more than 64 rows
                                          (9, 8, 5000, 512, 1.0), (40, 4, 4097, 256, 0.7),
                                          (33, 2, 20000, 1024, 2.0)])
