@@ -97,28 +97,28 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_075_193, write=73_920, source="int4vh.hip",
-                     source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "full_t8": dict(read=390_385_235, write=41_088, source="int4vh.hip",
-                    source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "two_blocks_t16": dict(read=393_060_194, write=74_048, source="int4vh.hip",
-                           source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "batch": dict(read=683_933_418, write=1_062_176, source="int4vh.hip",
-                  source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "draft_vocab": dict(read=21_351_003, write=17_536, source="int4vh.hip",
-                        source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "shard_t16": dict(read=50_771_309, write=74_944, source="int4vh.hip",
-                      source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "full_t16_top16": dict(read=391_709_262, write=568_576, source="int4vh.hip",
-                           source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "full_t16_top0": dict(read=391_496_194, write=358_912, source="int4vh.hip",
-                          source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "two_blocks_t16_top16": dict(read=393_664_427, write=570_816, source="int4vh.hip",
-                                 source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "batch_top16": dict(read=684_049_022, write=159_546_336, source="int4vh.hip",
-                        source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
-    "batch_top0": dict(read=684_044_823, write=156_644_640, source="int4vh.hip",
-                       source_sha256="2fcaabad1b898f3a2fc6875795201593a6583a9739bf157615f68d0d311fe08e"),
+    "full_t16": dict(read=391_066_615, write=73_920, source="int4vh.hip",
+                     source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "full_t8": dict(read=390_394_496, write=41_088, source="int4vh.hip",
+                    source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "two_blocks_t16": dict(read=393_072_190, write=74_048, source="int4vh.hip",
+                           source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "batch": dict(read=683_946_686, write=1_062_176, source="int4vh.hip",
+                  source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "draft_vocab": dict(read=21_336_722, write=17_536, source="int4vh.hip",
+                        source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "shard_t16": dict(read=50_763_235, write=74_944, source="int4vh.hip",
+                      source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "full_t16_top16": dict(read=391_698_582, write=568_576, source="int4vh.hip",
+                           source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "full_t16_top0": dict(read=391_505_209, write=358_912, source="int4vh.hip",
+                          source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "two_blocks_t16_top16": dict(read=393_677_025, write=570_816, source="int4vh.hip",
+                                 source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "batch_top16": dict(read=684_037_802, write=159_542_453, source="int4vh.hip",
+                        source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "batch_top0": dict(read=684_024_649, write=156_644_640, source="int4vh.hip",
+                       source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="9626a04fb5fe559ea2d9ed02d060f37f8d35b7e5fb71bbd087b08539e02acfef"),
 }

@@ -1052,13 +1052,31 @@ verify_kernel(Args a)
     float lm = -__builtin_huge_valf(), ls = 0.0f;
     const float zscale = 1.4426950408889634f / a.tau;
     int cnt0 = 0, cnt1 = 0;             // buffered candidates of the wave's two tokens (wave-uniform)
-    // sort the buffered candidates of both tokens into their lists (all lanes)
+    // A flush of the buffered candidates into the lists is a chain of
+    // dependent cross-lane steps that holds the whole workgroup at the next
+    // barrier, so it is split over two tiles: the buffer is sorted on one
+    // tile and merged into the lists at the start of the next.  Until then
+    // the bar a key must pass is the older, lower one: a superset of the
+    // candidates, so the lists stay exact.  (pend is wave-uniform.)
+    unsigned long long srt_pend = 0ull;
+    bool pend = false;
+    auto merge_pending = [&]() {
+        if constexpr (kCBuf) {
+            if (pend) {
+                dl = dlist_merge(dl, key_dpp<0x140>(srt_pend), lane);      // row_mirror: rank 15-j
+                pend = false;
+            }
+        }
+    };
+    // sort the buffered candidates of both tokens (all lanes); the merge
+    // follows on the next tile
     auto flush_cand = [&]() {
         if constexpr (kCBuf) {
+            merge_pending();
             const int cnt = lane < 16 ? cnt0 : cnt1;
             const unsigned long long v = (lane < 32 && n16 < cnt) ? lds.cbuf[wave][(lane >> 4) & 1][n16] : 0ull;
-            const unsigned long long srt = row_sort16(v, n16);
-            dl = dlist_merge(dl, key_dpp<0x140>(srt), lane);      // row_mirror: rank 15-j
+            srt_pend = row_sort16(v, n16);
+            pend = true;
             cnt0 = 0;
             cnt1 = 0;
         }
@@ -1112,9 +1130,10 @@ verify_kernel(Args a)
             // sorted, are the lists (wave-uniform control flow)
             dl = row_sort16(key, n16);
         } else if constexpr (kCBuf) {
+            merge_pending();                       // the previous tile's sorted flush, if any
             // the tile's keys that beat the list's last kept rank go to the
-            // token's candidate buffer; a full buffer is sorted and merged
-            // into the list first (wave-uniform control flow)
+            // token's candidate buffer; a full buffer is sorted first (and
+            // merged on the next tile) (wave-uniform control flow)
             const unsigned long long th0 = key_readlane(dl, kTopK - 1);
             const unsigned long long th1 = key_readlane(dl, 16 + kTopK - 1);
             const bool is_cand = key > (lane < 16 ? th0 : th1);
@@ -1236,6 +1255,7 @@ verify_kernel(Args a)
     reduce_tile(n_my - 1);
     if (cnt0 + cnt1 > 0)
         flush_cand();
+    merge_pending();
 
     // ---------------- per-workgroup best per token
     if constexpr (kTopK == 0)
