@@ -97,28 +97,28 @@ def cpu_baseline(cfg, head, trials, n_threads, top_k=None, temperature=1.0, vmap
 # entry holds the SHA-256 of the kernel source it was measured on: once the
 # source changes the entry no longer applies and `traffic` is null.
 MEASURED_TRAFFIC = {
-    "full_t16": dict(read=391_066_615, write=73_920, source="int4vh.hip",
-                     source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "full_t8": dict(read=390_394_496, write=41_088, source="int4vh.hip",
-                    source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "two_blocks_t16": dict(read=393_072_190, write=74_048, source="int4vh.hip",
-                           source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "batch": dict(read=683_946_686, write=1_062_176, source="int4vh.hip",
-                  source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "draft_vocab": dict(read=21_336_722, write=17_536, source="int4vh.hip",
-                        source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "shard_t16": dict(read=50_763_235, write=74_944, source="int4vh.hip",
-                      source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "full_t16_top16": dict(read=391_698_582, write=568_576, source="int4vh.hip",
-                           source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "full_t16_top0": dict(read=391_505_209, write=358_912, source="int4vh.hip",
-                          source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "two_blocks_t16_top16": dict(read=393_677_025, write=570_816, source="int4vh.hip",
-                                 source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "batch_top16": dict(read=684_037_802, write=159_542_453, source="int4vh.hip",
-                        source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
-    "batch_top0": dict(read=684_024_649, write=156_644_640, source="int4vh.hip",
-                       source_sha256="7d1a92af75dcb17266274baa255d47c71e02a45d47ebc64ce7e1484ce7feaa46"),
+    "full_t16": dict(read=391_060_135, write=73_920, source="int4vh.hip",
+                     source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "full_t8": dict(read=390_392_529, write=41_088, source="int4vh.hip",
+                    source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "two_blocks_t16": dict(read=393_049_627, write=74_048, source="int4vh.hip",
+                           source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "batch": dict(read=683_951_487, write=1_062_176, source="int4vh.hip",
+                  source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "draft_vocab": dict(read=21_350_396, write=17_536, source="int4vh.hip",
+                        source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "shard_t16": dict(read=50_761_953, write=74_944, source="int4vh.hip",
+                      source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "full_t16_top16": dict(read=391_712_757, write=568_576, source="int4vh.hip",
+                           source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "full_t16_top0": dict(read=391_481_381, write=358_912, source="int4vh.hip",
+                          source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "two_blocks_t16_top16": dict(read=393_676_928, write=570_816, source="int4vh.hip",
+                                 source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "batch_top16": dict(read=684_045_968, write=159_548_356, source="int4vh.hip",
+                        source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
+    "batch_top0": dict(read=684_042_427, write=156_644_640, source="int4vh.hip",
+                       source_sha256="578e0dc5ae34e588a913373167627327a2538b4141a10d5cb61fc0c3b60256ba"),
     "requant": dict(read=1_555_894_656, write=388_956_160, source="requant.hip",
                     source_sha256="9626a04fb5fe559ea2d9ed02d060f37f8d35b7e5fb71bbd087b08539e02acfef"),
 }

@@ -1115,7 +1115,7 @@ verify_kernel(Args a)
                 if constexpr (kTopK > 0) {
                     key = order_key(val, v);
                     if constexpr (kLse)
-                        lse_combine(lm, ls, val * zscale, 1.0f);
+                        lse_add(lm, ls, val * zscale);      // one exp2 per logit
                     if (kLse && v == my_draft) {      // one lane of one workgroup per token
                         __hip_atomic_store(&a.draft_logit[grow], val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         __hip_atomic_store(&a.draft_seen[grow], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
